@@ -1,0 +1,108 @@
+"""Seeded synthetic workloads for the MoE layer.
+
+This module only draws random inputs; it holds none of the layer's arithmetic
+(no routing, no softmax, no projection).  Both the HIP path and the CPU checker
+receive the tensors it returns, bit for bit.
+
+The five workloads mirror the layer shapes the SonicMoE pages benchmark on: a
+fine-grained 7B MoE with n = 256 (ICLR-2026 notes, main results), a
+high-granularity layer (d/n = 16) and a high-sparsity layer (128 tokens per
+expert on average), plus a tiny and a small layer for checking.  The pages name
+no dataset for these kernel benchmarks, so seeded Gaussian data of these shapes
+stands in for them.
+
+Recipe (numpy PCG64 ``default_rng(seed)``, draws in float32, in the order X,
+W1, W2, router, bias, dO):
+  * tiny: X, W1, W2 and router weights W_r ~ N(0, 0.02^2); logits = X W_r
+    computed in float64 from the (rounded) X and stored as float32.
+  * others: X ~ N(0, 1); W1 ~ N(0, 1/d); W2 ~ N(0, 1/n) (std 1/sqrt(fan_in));
+    logits z ~ N(0, 1) i.i.d., plus a per-expert bias b_e for two of them:
+    b ~ N(0, 0.5^2) (the 7B layer), or b_e = -1.1 ln(pi_e) with pi a seeded
+    permutation of 1..E (high sparsity; softmax of the bias is Zipf(1.1)
+    over expert ranks).
+  * dO ~ N(0, 1).
+bf16 inputs are the float32 draws rounded to nearest even; logits stay fp32.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    name: str
+    T: int      # tokens
+    d: int      # model dim
+    n: int      # expert intermediate dim (W1 is d x 2n for SwiGLU)
+    E: int      # experts
+    K: int      # experts per token (top-K)
+    M: int      # M_tile the counts are rounded to
+    init: str   # "tiny" or "fan_in"
+    logits: str  # "router", "iid", "normal_bias" or "zipf_bias"
+
+    @property
+    def flops(self):
+        """18 T n K d: what one forward+backward step is credited with."""
+        return 18 * self.T * self.n * self.K * self.d
+
+
+SHAPES = {
+    s.name: s
+    for s in [
+        LayerShape("tiny", 256, 128, 64, 8, 2, 16, "tiny", "router"),
+        LayerShape("small", 4096, 768, 256, 64, 8, 128, "fan_in", "iid"),
+        LayerShape("7b", 16384, 1536, 256, 128, 8, 128, "fan_in", "normal_bias"),
+        LayerShape("high_g", 16384, 4096, 256, 256, 16, 128, "fan_in", "iid"),
+        LayerShape("high_sparsity", 8192, 2048, 384, 512, 8, 128, "fan_in",
+                   "zipf_bias"),
+    ]
+}
+
+
+def _cast(a32: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32))
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
+def make_layer_inputs(shape: LayerShape | str, dtype=torch.bfloat16, seed=0,
+                      T=None):
+    """Returns CPU tensors X [T, d], W1 [E, d, 2n], W2 [E, n, d] (dtype),
+    logits [T, E] (float32) and dO [T, d] (dtype).  ``T`` overrides the
+    token count (same per-token recipe) for reduced-size checks."""
+    if isinstance(shape, str):
+        shape = SHAPES[shape]
+    T = shape.T if T is None else T
+    d, n, E = shape.d, shape.n, shape.E
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    if shape.init == "tiny":
+        X = rng.standard_normal((T, d), dtype=f32) * f32(0.02)
+        W1 = rng.standard_normal((E, d, 2 * n), dtype=f32) * f32(0.02)
+        W2 = rng.standard_normal((E, n, d), dtype=f32) * f32(0.02)
+    else:
+        X = rng.standard_normal((T, d), dtype=f32)
+        W1 = rng.standard_normal((E, d, 2 * n), dtype=f32) * f32(1 / np.sqrt(d))
+        W2 = rng.standard_normal((E, n, d), dtype=f32) * f32(1 / np.sqrt(n))
+    Xt = _cast(X, dtype)
+    if shape.logits == "router":
+        Wr = rng.standard_normal((d, E), dtype=f32) * f32(0.02)
+        logits = (Xt.double().numpy() @ Wr.astype(np.float64)).astype(f32)
+    else:
+        logits = rng.standard_normal((T, E), dtype=f32)
+        if shape.logits == "normal_bias":
+            logits = logits + rng.standard_normal(E, dtype=f32) * f32(0.5)
+        elif shape.logits == "zipf_bias":
+            ranks = rng.permutation(E) + 1
+            logits = logits + (-1.1 * np.log(ranks)).astype(f32)
+    dO = rng.standard_normal((T, d), dtype=f32)
+    return {
+        "X": Xt,
+        "W1": _cast(W1, dtype),
+        "W2": _cast(W2, dtype),
+        "logits": torch.from_numpy(np.ascontiguousarray(logits, dtype=f32)),
+        "dO": _cast(dO, dtype),
+    }

@@ -1,0 +1,192 @@
+"""Pins for the oracle's routing: top-K token choice and token rounding.
+
+Each check is independent of the oracle's own code: pure-Python brute force,
+hand-worked fixtures (tests/golden/, derived from the rule in the SonicMoE
+ICLR-2026 notes, key design 1), special cases with known answers, and the
+invariants the notes state for token rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as orc
+from fine_grained_mixture_amd.inputs import SHAPES, make_layer_inputs
+from tests.golden_io import rounding_cases, worked_example
+
+
+def brute_topk(row, K):
+    return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:K]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_topk_matches_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    T, E, K = 40, 9, 3
+    # small integer-valued logits force many exact ties
+    logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    got = orc.topk_token_choice(logits, K)
+    for t in range(T):
+        assert list(got[t]) == brute_topk(logits[t], K)
+
+
+def test_topk_all_experts():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((17, 5)).astype(np.float32)
+    rt = orc.route(logits, K=5, M=4, mode=orc.TC)
+    assert np.all(rt.tc_counts == 17)
+    for e in range(5):
+        a, b = rt.expert_offsets[e], rt.expert_offsets[e + 1]
+        assert list(rt.slot_token[a:b]) == list(range(17))
+
+
+def test_softmax_closed_form():
+    logits = np.array([[0.0, math.log(2.0), math.log(5.0)]], dtype=np.float32)
+    p = orc.softmax_probs(logits)
+    # exp of the fp32-rounded logs
+    ex = [math.exp(float(np.float32(v))) for v in logits[0]]
+    np.testing.assert_allclose(p[0], np.array(ex) / sum(ex), rtol=1e-15)
+
+
+@pytest.mark.parametrize("f,M,T,expected", rounding_cases())
+def test_rounding_rule_golden(f, M, T, expected):
+    assert int(orc.round_counts([f], M, T, orc.TR)[0]) == expected
+    assert int(orc.round_counts([f], M, T, orc.TC)[0]) == f
+
+
+def test_worked_example_golden():
+    g = worked_example()
+    tr = orc.route(g["logits"], K=1, M=4, mode=orc.TR)
+    assert list(tr.tc_counts) == list(g["tc_counts"])
+    assert list(tr.counts) == list(g["tr_counts"])
+    assert list(tr.slot_token) == list(g["tr_slot_token"])
+    assert list(tr.token_offsets) == list(g["tr_token_offsets"])
+    assert list(tr.token_slots) == list(g["tr_token_slots"])
+    # padded pair (t6, e0) carries its own softmax probability
+    e = math.e
+    want = math.sqrt(e) / (math.sqrt(e) + 1.0 + e)
+    assert tr.slot_weight[3] == pytest.approx(want, rel=1e-7)
+    tc = orc.route(g["logits"], K=1, M=4, mode=orc.TC)
+    assert list(tc.slot_token) == list(g["tc_slot_token"])
+    assert list(tc.counts) == list(g["tc_counts"])
+
+
+def _tr_reference_sets(p, is_tc, r):
+    """Set-based restatement: all TC tokens plus the best EC candidates when
+    padding, or the best TC tokens when dropping."""
+    T, E = p.shape
+    sets = []
+    for e in range(E):
+        tc = [t for t in range(T) if is_tc[t, e]]
+        ec = [t for t in range(T) if not is_tc[t, e]]
+        best = lambda ts: sorted(ts, key=lambda t: (-p[t, e], t))
+        if r[e] >= len(tc):
+            chosen = tc + best(ec)[: r[e] - len(tc)]
+        else:
+            chosen = best(tc)[: r[e]]
+        sets.append(sorted(chosen))
+    return sets
+
+
+def check_tr_invariants(logits, K, M):
+    T, E = logits.shape
+    tc = orc.route(logits, K, M, orc.TC)
+    tr = orc.route(logits, K, M, orc.TR)
+    f, r = tr.tc_counts, tr.counts
+    assert np.array_equal(f, tc.counts)
+    assert np.all(r % M == 0)                       # multiples of the tile
+    assert np.all(np.abs(r - f) < M)                # within one tile of TC
+    assert np.all(2 * np.abs(r - f) <= M)           # nearest rounding
+    assert abs(int(r.sum()) - int(f.sum())) <= E * M // 2
+    p = tr.probs
+    is_tc = np.zeros((T, E), bool)
+    is_tc[np.arange(T)[:, None], tr.topk_ids] = True
+    for e in range(E):
+        a, b = tr.expert_offsets[e], tr.expert_offsets[e + 1]
+        kept = set(tr.slot_token[a:b].tolist())
+        tcs = set(np.nonzero(is_tc[:, e])[0].tolist())
+        assert len(kept) == r[e]
+        if r[e] >= f[e]:
+            assert tcs <= kept                      # TC kept before EC
+        else:
+            assert kept < tcs                       # only TC tokens dropped
+        dropped = [t for t in range(T) if t not in kept]
+        if kept and dropped:
+            key = lambda t: (is_tc[t, e], p[t, e], -t)
+            assert min(key(t) for t in kept) > max(key(t) for t in dropped)
+        # slots of an expert ascend by token
+        assert np.all(np.diff(tr.slot_token[a:b]) > 0)
+        assert np.all(tr.slot_weight[a:b] == p[tr.slot_token[a:b], e])
+    ref = _tr_reference_sets(p, is_tc, r)
+    for e in range(E):
+        a, b = tr.expert_offsets[e], tr.expert_offsets[e + 1]
+        assert tr.slot_token[a:b].tolist() == ref[e]
+    # token CSR lists every slot once, by ascending expert
+    assert tr.token_offsets[-1] == tr.S
+    assert sorted(tr.token_slots.tolist()) == list(range(tr.S))
+    for t in range(T):
+        sl = tr.token_slots[tr.token_offsets[t]:tr.token_offsets[t + 1]]
+        assert np.all(tr.slot_token[sl] == t)
+        assert np.all(np.diff(tr.slot_expert[sl]) > 0)
+    return tc, tr
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("T,E,K,M", [(64, 6, 2, 8), (50, 7, 3, 4), (33, 4, 1, 16),
+                                     (128, 16, 4, 16)])
+def test_tr_invariants_random(seed, T, E, K, M):
+    rng = np.random.default_rng(seed)
+    logits = (rng.standard_normal((T, E)) + rng.standard_normal(E)).astype(np.float32)
+    check_tr_invariants(logits, K, M)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tr_invariants_tiny_shape(seed):
+    import torch
+    inp = make_layer_inputs("tiny", dtype=torch.bfloat16, seed=seed)
+    s = SHAPES["tiny"]
+    check_tr_invariants(inp["logits"].numpy(), s.K, s.M)
+
+
+def test_tr_m1_equals_tc():
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((70, 9)).astype(np.float32)
+    tc = orc.route(logits, 3, 1, orc.TC)
+    tr = orc.route(logits, 3, 1, orc.TR)
+    assert np.array_equal(tc.slot_token, tr.slot_token)
+    assert np.array_equal(tc.expert_offsets, tr.expert_offsets)
+
+
+def test_tr_multiples_equal_tc():
+    # 4 experts, K=1, tokens split 8/8/4/12 by a fixed argmax: every f_e is a
+    # multiple of M=4, so rounding changes nothing.
+    owners = [0] * 8 + [1] * 8 + [2] * 4 + [3] * 12
+    rng = np.random.default_rng(6)
+    logits = rng.uniform(-1, 0, size=(len(owners), 4)).astype(np.float32)
+    for t, e in enumerate(owners):
+        logits[t, e] = 2.0
+    tc = orc.route(logits, 1, 4, orc.TC)
+    tr = orc.route(logits, 1, 4, orc.TR)
+    assert list(tc.counts) == [8, 8, 4, 12]
+    assert np.array_equal(tc.slot_token, tr.slot_token)
+
+
+def test_tr_drops_leave_tokens_without_expert():
+    g = worked_example()
+    tr = orc.route(g["logits"], K=1, M=4, mode=orc.TR)
+    assert tr.token_offsets[4] - tr.token_offsets[3] == 0
+
+
+def test_tr_equal_scores_go_to_lower_token():
+    # Pad case: t0..t2 pick e0 (f=3, M=4 -> r=4); t3..t7 have identical rows,
+    # so their p[t, 0] tie exactly and the pad must take the lowest token, t3.
+    rows = [[2.0, 0.0]] * 3 + [[0.0, 1.0]] * 5
+    tr = orc.route(np.array(rows, np.float32), K=1, M=4, mode=orc.TR)
+    assert list(tr.counts) == [4, 4]
+    assert tr.slot_token[:4].tolist() == [0, 1, 2, 3]
+    # Drop case: t0..t4 pick e0 with equal rows (f=5 -> r=4): the highest
+    # token, t4, is the one dropped.
+    rows = [[2.0, 0.0]] * 5 + [[0.0, 1.0]] * 3
+    tr = orc.route(np.array(rows, np.float32), K=1, M=4, mode=orc.TR)
+    assert list(tr.counts) == [4, 4]
+    assert tr.slot_token[:4].tolist() == [0, 1, 2, 3]
