@@ -1,0 +1,241 @@
+"""Benchmark of the MoE layer forward+backward on one MI355X.
+
+A step is one pass of the whole path on one batch of synthetic input:
+moe_route (top-K + token rounding) -> moe_fwd (up-proj + SwiGLU, down-proj,
+aggregation) -> moe_bwd (dH + dS, dX-tilde, dX aggregation, dW1, dW2).
+The step is credited with 6TnKd forward + 12TnKd backward FLOPs.
+
+Prints ONE JSON line.  `roofline` describes the kernel with the largest
+average duration, timed live with HIP events recorded on the library's stream
+between its launches; `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload (a subset of the experts) on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 7b]
+                       [--mode tr|tc] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fine_grained_mixture_amd import moe  # noqa: E402
+from fine_grained_mixture_amd.inputs import SHAPES, make_layer_inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def kernel_model(name, sh, S, esz=2):
+    """Algorithmic FLOPs and HBM bytes of one launch of each kernel: the
+    operands the method must move once (gathered rows counted once per slot,
+    weights once, transients written and read once), no padded work."""
+    T, d, n, E = sh.T, sh.d, sh.n, sh.E
+    idx = 4 * S  # one int32 per slot
+    m = {
+        "up_swiglu": (4 * S * d * n, esz * (S * d + E * d * 2 * n + S * 2 * n + S * n) + idx),
+        "down": (2 * S * n * d, esz * (S * n + E * n * d + S * d)),
+        "aggregate_O": (2 * S * d, esz * (S * d + T * d) + 2 * idx + 4 * T),
+        "dh": (2 * S * d * n, esz * (S * d + E * n * d + S * 2 * n + S * 2 * n + S * n)
+               + 4 * S + 2 * idx),
+        "dxt": (4 * S * n * d, esz * (S * 2 * n + E * d * 2 * n + S * d)),
+        "aggregate_dX": (S * d, esz * (S * d + T * d) + idx + 4 * T),
+        "dw1": (4 * S * d * n, esz * (S * d + S * 2 * n + E * d * 2 * n) + idx),
+        "dw2": (2 * S * n * d, esz * (S * n + S * d + E * n * d) + idx),
+    }
+    return m.get(name)
+
+
+def restrict_routing(rt, keep):
+    """Oracle routing restricted to the experts in `keep` (the others empty)."""
+    from oracle import moe_oracle as orc
+
+    E = len(rt.counts)
+    sel = np.isin(rt.slot_expert, keep)
+    slot_token = rt.slot_token[sel]
+    slot_expert = rt.slot_expert[sel]
+    counts = np.bincount(slot_expert, minlength=E)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    T = len(rt.token_offsets) - 1
+    order = np.argsort(slot_token, kind="stable")
+    toff = np.zeros(T + 1, np.int64)
+    toff[1:] = np.cumsum(np.bincount(slot_token, minlength=T))
+    return orc.Routing(rt.topk_ids, rt.tc_counts, counts, offsets, slot_token, slot_expert,
+                       rt.slot_weight[sel], toff, order, rt.probs)
+
+
+def cpu_baseline(sh, inp, mode, target_s=15.0):
+    """fp64 oracle on a sample of experts: route (full), forward, backward."""
+    from oracle import moe_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(i.get("num_threads", 0) for i in threadpool_info()
+                      if i.get("user_api") == "blas") or os.cpu_count()
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    a = {k: v.float().numpy().astype(np.float64) for k, v in inp.items() if k != "logits"}
+    logits = inp["logits"].numpy()
+    t0 = time.perf_counter()
+    rt = orc.route(logits, sh.K, sh.M, orc.TR if mode == "tr" else orc.TC)
+    t_route = time.perf_counter() - t0
+    # Grow the expert sample until the timed fwd+bwd takes a few seconds.
+    order = np.argsort(-rt.counts, kind="stable")
+    n_exp, spent, best = 2, 0.0, None
+    while True:
+        keep = order[:: max(1, len(order) // n_exp)][:n_exp]
+        sub = restrict_routing(rt, keep)
+        t0 = time.perf_counter()
+        _, c = orc.forward(a["X"], a["W1"], a["W2"], sub)
+        orc.backward_minimal(a["dO"], a["X"], c["H"], a["W1"], a["W2"], sub)
+        dt = time.perf_counter() - t0
+        spent += dt
+        best = (sub.S, dt, len(keep))
+        if dt > target_s / 3 or n_exp >= len(order) or spent > target_s:
+            break
+        n_exp = min(len(order), n_exp * 2)
+    S_s, dt, ne = best
+    flops = 18 * S_s * sh.n * sh.d
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle: full routing ({t_route:.2f} s) + forward and minimal "
+                  f"backward over {ne} of {sh.E} experts ({S_s} of {rt.S} slots, "
+                  f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s), scaled to TFLOPS",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
+    ap.add_argument("--mode", default="tr", choices=["tr", "tc"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    sh = SHAPES[args.config]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)
+    X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
+    p = moe.problem(sh.T, sh.d, sh.n, sh.E, sh.K, sh.M, torch.bfloat16, args.mode)
+    sz = moe.sizes(p)
+    rt = moe.alloc_routing(p, dev)
+    ws_r = moe.workspace(sz.ws_route, dev)
+    ws_f = moe.workspace(sz.ws_fwd, dev)
+    ws_b = moe.workspace(sz.ws_bwd, dev)
+    O = torch.empty(sh.T, sh.d, dtype=torch.bfloat16, device=dev)
+    H = torch.empty(sz.slot_cap, 2 * sh.n, dtype=torch.bfloat16, device=dev)
+    grads = (torch.empty_like(X), torch.empty_like(W1), torch.empty_like(W2),
+             torch.empty(sz.slot_cap, dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    names = [f"route:{k}" for k in moe.ROUTE_KERNELS] + list(moe.FWD_KERNELS) + \
+        list(moe.BWD_KERNELS)
+    def mk(k):
+        # torch creates an event's handle on its first record
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    def step(ev=None):
+        e_r, e_f, e_b = ev if ev else (None, None, None)
+        moe.route(p, lg, rt=rt, ws=ws_r, stream=stream, events=e_r)
+        moe.forward(p, X, W1, W2, rt, out=(O, H), ws=ws_f, stream=stream, events=e_f)
+        moe.backward(p, dO, X, H, W1, W2, rt, out=grads, ws=ws_b, stream=stream, events=e_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(mk(7), mk(4), mk(6)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    per = np.zeros(len(names))
+    for e_r, e_f, e_b in evs:
+        d = [a.elapsed_time(b) for group in (e_r, e_f, e_b) for a, b in zip(group, group[1:])]
+        per += np.array(d)
+    per /= args.steps
+    S = int(rt.totals[0].item())
+    flops = sh.flops
+    tflops = flops / (ms / 1e3) / 1e12
+
+    # roofline of the dominant kernel
+    dom = int(np.argmax(per))
+    dname = names[dom]
+    f_k, b_k = kernel_model(dname, sh, S) or (0, 0)
+    t_mfma, t_hbm = f_k / (PEAK_BF16_TFLOPS * 1e12), b_k / (PEAK_HBM_GBS * 1e9)
+    dur = per[dom] / 1e3
+    if f_k and t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": f_k / dur / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": b_k / dur / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dname
+    roof["avg_us"] = per[dom] * 1e3
+
+    kernels = {}
+    for k, t in zip(names, per):
+        fk, bk = kernel_model(k, sh, S) or (0, 0)
+        kernels[k] = {"us": round(t * 1e3, 2)}
+        if fk:
+            kernels[k]["tflops"] = round(fk / (t / 1e3) / 1e12, 1)
+        if bk:
+            kernels[k]["gbs"] = round(bk / (t / 1e3) / 1e9, 1)
+
+    out = {
+        "metric": "MoE layer fwd+bwd TFLOPS (bf16) + % MFMA peak, T=16k d=1536 E=128 K=8",
+        "value": tflops,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{sh.name} MoE layer fwd+bwd, {args.mode.upper()} routing",
+                   "T": sh.T, "d": sh.d, "n": sh.n, "E": sh.E, "K": sh.K, "M_tile": sh.M,
+                   "slots": S, "parallelism": "single GPU"},
+        "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "roofline": roof,
+        "kernels_us": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(sh, inp, args.mode)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

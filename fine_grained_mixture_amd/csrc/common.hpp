@@ -1,0 +1,175 @@
+// Shared device-side definitions for the gfx950 MoE kernels: storage types,
+// bf16 conversion, MFMA wrappers and the routing-workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kTileM = 128;  // rows per M tile of the grouped GEMMs
+
+// ---------------------------------------------------------------------------
+// Conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <class T> struct Elem;
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(bf16_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static bf16_t store(float v) { return f32_to_bf16(v); }
+  // value after one round trip through storage precision
+  __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(float v) { return v; }
+  __device__ __forceinline__ static float store(float v) { return v; }
+  __device__ __forceinline__ static float round(float v) { return v; }
+};
+
+// Eight consecutive elements of T ("an octet"): 16 B for bf16, 32 B for fp32.
+template <class T> struct Oct {
+  static constexpr int kWords = sizeof(T) * 2;  // 32-bit words
+  uint32_t w[kWords];
+};
+
+template <class T>
+__device__ __forceinline__ void oct_zero(Oct<T>& o) {
+#pragma unroll
+  for (int i = 0; i < Oct<T>::kWords; ++i) o.w[i] = 0u;
+}
+
+template <class T>
+__device__ __forceinline__ void oct_load(Oct<T>& o, const T* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < Oct<T>::kWords / 4; ++i) {
+    uint4 v = q[i];
+    o.w[4 * i + 0] = v.x; o.w[4 * i + 1] = v.y; o.w[4 * i + 2] = v.z; o.w[4 * i + 3] = v.w;
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void oct_store(T* p, const Oct<T>& o) {
+  uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < Oct<T>::kWords / 4; ++i)
+    q[i] = make_uint4(o.w[4 * i + 0], o.w[4 * i + 1], o.w[4 * i + 2], o.w[4 * i + 3]);
+}
+
+template <class T>
+__device__ __forceinline__ float oct_get(const Oct<T>& o, int i);
+template <>
+__device__ __forceinline__ float oct_get<bf16_t>(const Oct<bf16_t>& o, int i) {
+  uint32_t w = o.w[i >> 1];
+  return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+template <>
+__device__ __forceinline__ float oct_get<float>(const Oct<float>& o, int i) {
+  return __uint_as_float(o.w[i]);
+}
+
+// Transpose an 8x8 block: out[c] element k = in[k] element c.
+__device__ __forceinline__ void oct_transpose(Oct<bf16_t> (&out)[8], const Oct<bf16_t> (&in)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const uint32_t a = in[2 * kp].w[c >> 1];
+      const uint32_t b = in[2 * kp + 1].w[c >> 1];
+      // low half of the output word from row 2kp, high half from row 2kp+1
+      out[c].w[kp] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+__device__ __forceinline__ void oct_transpose(Oct<float> (&out)[8], const Oct<float> (&in)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[c].w[k] = in[k].w[c];
+}
+
+// ---------------------------------------------------------------------------
+// MFMA: one 32x32 fp32 accumulator block += 16 k-values.
+//
+// Lane l supplies 8 k-values of row (l % 32) of each operand; lanes 0-31 and
+// 32-63 hold the two halves of the 16-wide k chunk.  The result element r of
+// lane l sits at row (r/4)*8 + (l/32)*4 + r%4 of the first operand and
+// column l % 32 of the second.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mma16(f32x16_t& acc, const Oct<bf16_t>& a, const Oct<bf16_t>& b) {
+  bf16x8_t va, vb;
+  __builtin_memcpy(&va, a.w, 16);
+  __builtin_memcpy(&vb, b.w, 16);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16_t& acc, const Oct<float>& a, const Oct<float>& b) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w[k]), __uint_as_float(b.w[k]),
+                                                 acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+template <class T>
+__host__ __device__ constexpr T cdiv(T a, T b) { return (a + b - 1) / b; }
+
+// Routing workspace layout (byte offsets), shared by the host code and the
+// routing kernels.
+struct RouteWs {
+  size_t keys;     // uint64 [E][T]  (is-token-choice << 63) | bits(p[t,e])
+  size_t bits_e;   // uint32 [E][nw] selection bitmap, expert-major (nw = ceil(T/32))
+  size_t bits_t;   // uint32 [T][W]  selection bitmap, token-major (W = ceil(E/32))
+  size_t wbase;    // int32  [E][nw] slots of expert e in words before w
+  size_t total;
+  __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
+  __host__ __device__ static RouteWs make(int64_t T, int64_t E) {
+    RouteWs w;
+    const int64_t nw = (T + 31) / 32, W = (E + 31) / 32;
+    size_t o = 0;
+    w.keys = o;   o = align(o + size_t(E) * T * 8);
+    w.bits_e = o; o = align(o + size_t(E) * nw * 4);
+    w.bits_t = o; o = align(o + size_t(T) * W * 4);
+    w.wbase = o;  o = align(o + size_t(E) * nw * 4);
+    w.total = o;
+    return w;
+  }
+};
+
+}  // namespace moe
+
+namespace moe {
+template <class T>
+__device__ __forceinline__ void oct_from(Oct<T>& o, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void oct_from<bf16_t>(Oct<bf16_t>& o, const float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o.w[i] = uint32_t(f32_to_bf16(v[2 * i])) | (uint32_t(f32_to_bf16(v[2 * i + 1])) << 16);
+}
+template <>
+__device__ __forceinline__ void oct_from<float>(Oct<float>& o, const float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o.w[i] = __float_as_uint(v[i]);
+}
+}  // namespace moe

@@ -1,0 +1,347 @@
+// Backward grouped GEMMs of the minimal-activation backward.
+//
+// SonicMoE ICLR-2026 notes (papernotes.org), key designs 2 and 3: only X, H
+// and the routing metadata survive the forward.  The dH kernel gathers dO
+// rows into its operand load and, in its epilogue, reloads H, recomputes
+// A = SwiGLU(H), and forms dS = <dA', A> together with dSwiGLU, so neither Y
+// nor dY is ever needed.  The weight gradients are varlen-K grouped GEMMs:
+// the contraction runs over each expert's own (gathered) token rows.
+//
+//   k_dh    dA' = dO[I_e] W2_e^T; dS, dH, s*A in the epilogue
+//   k_dxt   dX~_e = dH_e W1_e^T
+//   k_dw1   dW1_e = X[I_e]^T dH_e        (varlen-K)
+//   k_dw2   dW2_e = (s*A)_e^T dO[I_e]    (varlen-K)
+#include "gemm.hpp"
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
+
+// BN == n: one workgroup owns whole rows of dA', so the dS row sums stay
+// inside the workgroup and are written once, in a fixed order.
+template <class T, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(256) void k_dh(
+    const T* __restrict__ dO, const T* __restrict__ W2, const T* __restrict__ H,
+    T* __restrict__ dH, T* __restrict__ As, float* __restrict__ dS,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
+    const float* __restrict__ slot_weight, const int32_t* __restrict__ totals, int d) {
+  using Cfg = TileCfg<T, BM, BN, WGM, WGN>;
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  constexpr int n = BN, n2 = 2 * BN, SUB = kTileM / BM;
+  const int lin = xcd_tile(blockIdx.x, totals[1] * SUB);
+  if (lin < 0) return;
+  const int mt = lin / SUB;
+  const int e = tile_expert[mt], row0 = tile_row[mt] + (lin % SUB) * BM;
+  const int rend = expert_offsets[e + 1];
+  if (row0 >= rend) return;
+
+  DirectLoader<Cfg, BM> la;
+  la.init(dO, [&](int r) {
+    const int slot = row0 + r;
+    return slot < rend ? slot_token[slot] * d : -1;
+  });
+  DirectLoader<Cfg, BN> lb;
+  lb.init(W2 + int64_t(e) * n * d, [&](int j) { return j * d; });
+
+  Accum<Cfg> acc;
+  acc.init();
+  mainloop(acc, lds, d / Cfg::BK, la, lb);
+
+  float* red = reinterpret_cast<float*>(lds);  // [WGN][BM] partial row sums
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a) {
+    const int i = acc.row(a), slot = row0 + i;
+    float part = 0.0f;
+    if (slot < rend) {
+      const float s = slot_weight[slot];
+      const T* hrow = H + int64_t(slot) * n2;
+      T* dhrow = dH + int64_t(slot) * n2;
+      T* asrow = As + int64_t(slot) * n;
+#pragma unroll
+      for (int b = 0; b < Cfg::NB; ++b) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = acc.col(b, q);
+          T g4[4], u4[4], dg4[4], du4[4], as4[4];
+          __builtin_memcpy(g4, hrow + j, sizeof(g4));
+          __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float x = acc.acc[a][b][q * 4 + c];  // dA'
+            const float g = Elem<T>::load(g4[c]), u = Elem<T>::load(u4[c]);
+            const float sg = sigmoidf_(g), silu = g * sg;
+            const float av = silu * u;
+            part += x * av;
+            const float da = s * x;
+            dg4[c] = Elem<T>::store(da * u * sg * (1.0f + g * (1.0f - sg)));
+            du4[c] = Elem<T>::store(da * silu);
+            as4[c] = Elem<T>::store(s * av);
+          }
+          __builtin_memcpy(dhrow + j, dg4, sizeof(dg4));
+          __builtin_memcpy(dhrow + n + j, du4, sizeof(du4));
+          __builtin_memcpy(asrow + j, as4, sizeof(as4));
+        }
+      }
+    }
+    part += __shfl_xor(part, 32, 64);
+    if (acc.lane < 32) red[acc.wn * BM + i] = part;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < BM; i += 256) {
+    const int slot = row0 + i;
+    if (slot < rend) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WGN; ++w) sum += red[w * BM + i];
+      dS[slot] = sum;
+    }
+  }
+}
+
+template <class T, int BN>
+__global__ __launch_bounds__(256) void k_dxt(
+    const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
+    int n) {
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2>;
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  const int NT = d / BN, n2 = 2 * n;
+  const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
+  if (lin < 0) return;
+  const int mt = lin / NT, nt = lin % NT;
+  const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
+  const int j0 = nt * BN;
+
+  DirectLoader<Cfg, kTileM> la;
+  la.init(dH, [&](int r) {
+    const int slot = row0 + r;
+    return slot < rend ? slot * n2 : -1;
+  });
+  DirectLoader<Cfg, BN> lb;
+  lb.init(W1 + int64_t(e) * d * n2, [&](int c) { return (j0 + c) * n2; });
+
+  Accum<Cfg> acc;
+  acc.init();
+  mainloop(acc, lds, n2 / Cfg::BK, la, lb);
+
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a) {
+    const int slot = row0 + acc.row(a);
+    if (slot >= rend) continue;
+    T* orow = dXt + int64_t(slot) * d + j0;
+#pragma unroll
+    for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        T v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
+        __builtin_memcpy(orow + acc.col(b, q), v, sizeof(v));
+      }
+  }
+}
+
+// Varlen-K scheduling: expert_order lists experts by descending slot count.
+// Ranks q are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8),
+// and all PT output tiles of one expert stay on one XCD, so its gathered rows
+// are fetched into one L2; the largest experts start first.
+__device__ __forceinline__ bool varlen_k_tile(int b, int PT, int E, const int32_t* order,
+                                              int* e, int* tile) {
+  const int xcd = b % 8, local = b / 8;
+  const int q = (local / PT) * 8 + xcd;
+  if (q >= E) return false;
+  *e = order[q];
+  *tile = local % PT;
+  return true;
+}
+
+template <class Cfg>
+__device__ __forceinline__ void store_tile(const Accum<Cfg>& acc, typename Cfg::T* out, int ld) {
+  using T = typename Cfg::T;
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a) {
+    T* orow = out + int64_t(acc.row(a)) * ld;
+#pragma unroll
+    for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        T v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
+        __builtin_memcpy(orow + acc.col(b, q), v, sizeof(v));
+      }
+  }
+}
+
+template <class T, int BN>
+__global__ __launch_bounds__(256) void k_dw1(
+    const T* __restrict__ X, const T* __restrict__ dH, T* __restrict__ dW1,
+    const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
+    const int32_t* __restrict__ slot_token, int E, int d, int n) {
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2>;
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  const int n2 = 2 * n, TN = n2 / BN, PT = (d / kTileM) * TN;
+  int e, tile;
+  if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
+  const int i0 = (tile / TN) * kTileM, j0 = (tile % TN) * BN;
+  const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
+
+  auto la = make_trans<Cfg, kTileM>(
+      X,
+      [=](int s, int k) {
+        const int slot = kb + s * Cfg::BK + k;
+        return slot < ke ? slot_token[slot] * d : -1;
+      },
+      [=](int cg) { return i0 + cg * 8; });
+  auto lb = make_trans<Cfg, BN>(
+      dH,
+      [=](int s, int k) {
+        const int slot = kb + s * Cfg::BK + k;
+        return slot < ke ? slot * n2 : -1;
+      },
+      [=](int cg) { return j0 + cg * 8; });
+
+  Accum<Cfg> acc;
+  acc.init();
+  mainloop(acc, lds, (ke - kb + Cfg::BK - 1) / Cfg::BK, la, lb);
+  store_tile(acc, dW1 + (int64_t(e) * d + i0) * n2 + j0, n2);
+}
+
+template <class T, int BM, int BN>
+__global__ __launch_bounds__(256) void k_dw2(
+    const T* __restrict__ As, const T* __restrict__ dO, T* __restrict__ dW2,
+    const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
+    const int32_t* __restrict__ slot_token, int E, int d, int n) {
+  using Cfg = TileCfg<T, BM, BN, 2, 2>;
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  const int TN = d / BN, PT = (n / BM) * TN;
+  int e, tile;
+  if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
+  const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
+  const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
+
+  auto la = make_trans<Cfg, BM>(
+      As,
+      [=](int s, int k) {
+        const int slot = kb + s * Cfg::BK + k;
+        return slot < ke ? slot * n : -1;
+      },
+      [=](int cg) { return i0 + cg * 8; });
+  auto lb = make_trans<Cfg, BN>(
+      dO,
+      [=](int s, int k) {
+        const int slot = kb + s * Cfg::BK + k;
+        return slot < ke ? slot_token[slot] * d : -1;
+      },
+      [=](int cg) { return j0 + cg * 8; });
+
+  Accum<Cfg> acc;
+  acc.init();
+  mainloop(acc, lds, (ke - kb + Cfg::BK - 1) / Cfg::BK, la, lb);
+  store_tile(acc, dW2 + (int64_t(e) * n + i0) * d + j0, d);
+}
+
+template <class T>
+hipError_t dh_t(const LayerArgs& a, const void* dO, const void* W2, const void* H, void* dH,
+                void* As, float* dS, hipStream_t st) {
+  const T* o = static_cast<const T*>(dO);
+  const T* w = static_cast<const T*>(W2);
+  const T* h = static_cast<const T*>(H);
+  T* dh = static_cast<T*>(dH);
+  T* as = static_cast<T*>(As);
+#define MOE_DH(BM, BN, WGM, WGN)                                                              \
+  hipLaunchKernelGGL((k_dh<T, BM, BN, WGM, WGN>), dim3(grid_for(a.tile_cap * (kTileM / BM))), \
+                     dim3(256), 0, st, o, w, h, dh, as, dS, a.tile_expert, a.tile_row,        \
+                     a.expert_offsets, a.slot_token, a.slot_weight, a.totals, a.d)
+  switch (a.n) {
+    case 64: MOE_DH(128, 64, 4, 1); break;
+    case 128: MOE_DH(128, 128, 2, 2); break;
+    case 256: MOE_DH(128, 256, 2, 2); break;
+    case 384: MOE_DH(64, 384, 1, 4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DH
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t dxt_t(const LayerArgs& a, const void* dH, const void* W1, void* dXt, hipStream_t st) {
+  const T* dh = static_cast<const T*>(dH);
+  const T* w = static_cast<const T*>(W1);
+  T* o = static_cast<T*>(dXt);
+  if (sizeof(T) == 2 && a.d % 256 == 0)
+    hipLaunchKernelGGL((k_dxt<T, 256>), dim3(grid_for(a.tile_cap * (a.d / 256))), dim3(256), 0,
+                       st, dh, w, o, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
+                       a.n);
+  else
+    hipLaunchKernelGGL((k_dxt<T, 128>), dim3(grid_for(a.tile_cap * (a.d / 128))), dim3(256), 0,
+                       st, dh, w, o, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
+                       a.n);
+  return hipGetLastError();
+}
+
+inline unsigned varlen_k_grid(int E, int PT) { return unsigned(8 * ((E + 7) / 8) * PT); }
+
+template <class T>
+hipError_t dw1_t(const LayerArgs& a, const void* X, const void* dH, void* dW1, hipStream_t st) {
+  const T* x = static_cast<const T*>(X);
+  const T* dh = static_cast<const T*>(dH);
+  T* o = static_cast<T*>(dW1);
+  const int n2 = 2 * a.n;
+  if (sizeof(T) == 2 && n2 % 256 == 0)
+    hipLaunchKernelGGL((k_dw1<T, 256>), dim3(varlen_k_grid(a.E, (a.d / kTileM) * (n2 / 256))),
+                       dim3(256), 0, st, x, dh, o, a.expert_order, a.expert_offsets, a.slot_token,
+                       a.E, a.d, a.n);
+  else
+    hipLaunchKernelGGL((k_dw1<T, 128>), dim3(varlen_k_grid(a.E, (a.d / kTileM) * (n2 / 128))),
+                       dim3(256), 0, st, x, dh, o, a.expert_order, a.expert_offsets, a.slot_token,
+                       a.E, a.d, a.n);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t dw2_t(const LayerArgs& a, const void* As, const void* dO, void* dW2, hipStream_t st) {
+  const T* as = static_cast<const T*>(As);
+  const T* o = static_cast<const T*>(dO);
+  T* w = static_cast<T*>(dW2);
+#define MOE_DW2(BM, BN)                                                                      \
+  hipLaunchKernelGGL((k_dw2<T, BM, BN>), dim3(varlen_k_grid(a.E, (a.n / BM) * (a.d / BN))), \
+                     dim3(256), 0, st, as, o, w, a.expert_order, a.expert_offsets,          \
+                     a.slot_token, a.E, a.d, a.n)
+  const bool wide = sizeof(T) == 2 && a.d % 256 == 0;
+  if (a.n % 128 == 0) {
+    if (wide) MOE_DW2(128, 256);
+    else MOE_DW2(128, 128);
+  } else {
+    if (wide) MOE_DW2(64, 256);
+    else MOE_DW2(64, 128);
+  }
+#undef MOE_DW2
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const void* H, void* dH,
+                     void* As, float* dS, hipStream_t st) {
+  return a.f32 ? dh_t<float>(a, dO, W2, H, dH, As, dS, st)
+               : dh_t<bf16_t>(a, dO, W2, H, dH, As, dS, st);
+}
+hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
+                      hipStream_t st) {
+  return a.f32 ? dxt_t<float>(a, dH, W1, dXt, st) : dxt_t<bf16_t>(a, dH, W1, dXt, st);
+}
+hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1,
+                      hipStream_t st) {
+  return a.f32 ? dw1_t<float>(a, X, dH, dW1, st) : dw1_t<bf16_t>(a, X, dH, dW1, st);
+}
+hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2,
+                      hipStream_t st) {
+  return a.f32 ? dw2_t<float>(a, As, dO, dW2, st) : dw2_t<bf16_t>(a, As, dO, dW2, st);
+}
+
+}  // namespace moe

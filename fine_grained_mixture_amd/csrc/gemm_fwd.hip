@@ -1,0 +1,175 @@
+// Forward grouped GEMMs over the token-rounded slot layout.
+//
+// SonicMoE ICLR-2026 notes (papernotes.org), method > overall framework and
+// key design 2: the up-projection gathers each expert's token rows straight
+// from X into the GEMM operand (no separate gather pass) and applies SwiGLU
+// in its epilogue; the down-projection is a plain varlen-M grouped GEMM.
+//
+//   k_up_swiglu   H_e = X[I_e] W1_e; A_e = SiLU(H_gate) * H_up  -> H, A
+//   k_down        Y_e = A_e W2_e                               -> Y
+//
+// Both walk the device-side M-tile schedule written by the router (one tile
+// = up to 128 slot rows of a single expert); surplus workgroups of the
+// capacity-sized grid exit at once.
+#include "gemm.hpp"
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+// One workgroup computes a 128-row M tile against BN/2 gate columns and the
+// matching BN/2 up columns, so SiLU(gate) * up is formed in registers.
+template <class T, int BN>
+__global__ __launch_bounds__(256) void k_up_swiglu(
+    const T* __restrict__ X, const T* __restrict__ W1, T* __restrict__ H, T* __restrict__ Aact,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ totals, int d, int n) {
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2, true>;
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  constexpr int HALF = BN / 2;
+  const int NT = n / HALF;
+  const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
+  if (lin < 0) return;
+  const int mt = lin / NT, nt = lin % NT;
+  const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
+  const int j0 = nt * HALF, n2 = 2 * n;
+
+  DirectLoader<Cfg, kTileM> la;
+  la.init(X, [&](int r) {
+    const int slot = row0 + r;
+    return slot < rend ? slot_token[slot] * d : -1;
+  });
+  const T* w1 = W1 + int64_t(e) * d * n2;
+  auto lb = make_trans<Cfg, BN>(
+      w1, [=](int s, int k) { return (s * Cfg::BK + k) * n2; },
+      [=](int cg) { return cg * 8 < HALF ? j0 + cg * 8 : n + j0 + cg * 8 - HALF; });
+
+  Accum<Cfg> acc;
+  acc.init();
+  mainloop(acc, lds, d / Cfg::BK, la, lb);
+
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a) {
+    const int slot = row0 + acc.row(a);
+    if (slot >= rend) continue;
+    T* hrow = H + int64_t(slot) * n2;
+    T* arow = Aact + int64_t(slot) * n;
+#pragma unroll
+    for (int b = 0; b < Cfg::NB / 2; ++b) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + acc.col(b, q);  // gate column in [0, n)
+        T hg[4], hu[4], av[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float g = Elem<T>::round(acc.acc[a][b][q * 4 + c]);
+          const float u = Elem<T>::round(acc.acc[a][b + Cfg::NB / 2][q * 4 + c]);
+          hg[c] = Elem<T>::store(g);
+          hu[c] = Elem<T>::store(u);
+          av[c] = Elem<T>::store(g * sigmoidf_(g) * u);
+        }
+        __builtin_memcpy(hrow + j, hg, sizeof(hg));
+        __builtin_memcpy(hrow + n + j, hu, sizeof(hu));
+        __builtin_memcpy(arow + j, av, sizeof(av));
+      }
+    }
+  }
+}
+
+template <class T, int BN>
+__global__ __launch_bounds__(256) void k_down(
+    const T* __restrict__ Aact, const T* __restrict__ W2, T* __restrict__ Y,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
+    int n) {
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2>;
+  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  const int NT = d / BN;
+  const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
+  if (lin < 0) return;
+  const int mt = lin / NT, nt = lin % NT;
+  const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
+  const int j0 = nt * BN;
+
+  DirectLoader<Cfg, kTileM> la;
+  la.init(Aact, [&](int r) {
+    const int slot = row0 + r;
+    return slot < rend ? slot * n : -1;
+  });
+  const T* w2 = W2 + int64_t(e) * n * d;
+  auto lb = make_trans<Cfg, BN>(
+      w2, [=](int s, int k) { return (s * Cfg::BK + k) * d; }, [=](int cg) { return j0 + cg * 8; });
+
+  Accum<Cfg> acc;
+  acc.init();
+  mainloop(acc, lds, n / Cfg::BK, la, lb);
+
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a) {
+    const int slot = row0 + acc.row(a);
+    if (slot >= rend) continue;
+    T* yrow = Y + int64_t(slot) * d + j0;
+#pragma unroll
+    for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        T v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
+        __builtin_memcpy(yrow + acc.col(b, q), v, sizeof(v));
+      }
+  }
+}
+
+inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
+
+template <class T>
+hipError_t up_t(const LayerArgs& a, const void* X, const void* W1, void* H, void* Aact,
+                hipStream_t st) {
+  const T* x = static_cast<const T*>(X);
+  const T* w = static_cast<const T*>(W1);
+  T* h = static_cast<T*>(H);
+  T* av = static_cast<T*>(Aact);
+  if (sizeof(T) == 2 && a.n % 128 == 0) {
+    hipLaunchKernelGGL((k_up_swiglu<T, 256>), dim3(grid_for(a.tile_cap * (a.n / 128))), dim3(256),
+                       0, st, x, w, h, av, a.tile_expert, a.tile_row, a.expert_offsets,
+                       a.slot_token, a.totals, a.d, a.n);
+  } else {
+    hipLaunchKernelGGL((k_up_swiglu<T, 128>), dim3(grid_for(a.tile_cap * (a.n / 64))), dim3(256),
+                       0, st, x, w, h, av, a.tile_expert, a.tile_row, a.expert_offsets,
+                       a.slot_token, a.totals, a.d, a.n);
+  }
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t down_t(const LayerArgs& a, const void* Aact, const void* W2, void* Y, hipStream_t st) {
+  const T* av = static_cast<const T*>(Aact);
+  const T* w = static_cast<const T*>(W2);
+  T* y = static_cast<T*>(Y);
+  if (sizeof(T) == 2 && a.d % 256 == 0) {
+    hipLaunchKernelGGL((k_down<T, 256>), dim3(grid_for(a.tile_cap * (a.d / 256))), dim3(256), 0,
+                       st, av, w, y, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
+                       a.n);
+  } else {
+    hipLaunchKernelGGL((k_down<T, 128>), dim3(grid_for(a.tile_cap * (a.d / 128))), dim3(256), 0,
+                       st, av, w, y, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
+                       a.n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_up_swiglu(const LayerArgs& a, const void* X, const void* W1, void* H,
+                            void* Aact, hipStream_t st) {
+  return a.f32 ? up_t<float>(a, X, W1, H, Aact, st) : up_t<bf16_t>(a, X, W1, H, Aact, st);
+}
+
+hipError_t launch_down(const LayerArgs& a, const void* Aact, const void* W2, void* Y,
+                       hipStream_t st) {
+  return a.f32 ? down_t<float>(a, Aact, W2, Y, st) : down_t<bf16_t>(a, Aact, W2, Y, st);
+}
+
+}  // namespace moe

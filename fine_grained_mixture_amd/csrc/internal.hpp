@@ -1,0 +1,63 @@
+// Host-side launcher interfaces between the C ABI (moe_api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+// Records caller-supplied events between launches (see moe_trace in moe.h).
+struct TraceHook {
+  void** events = nullptr;
+  int count = 0;
+  void mark(hipStream_t st, int i) const {
+    if (events && i < count) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+  }
+};
+
+struct RouteArgs {
+  int T, E, K, M, mode;
+  const float* logits;
+  int32_t *tc_counts, *counts, *expert_offsets, *expert_order, *topk_ids;
+  int32_t* slot_token;
+  float* slot_weight;
+  int32_t *token_offsets, *token_slots, *tile_expert, *tile_row, *totals;
+  void* ws;
+};
+
+// Everything the grouped GEMMs and aggregation kernels need.
+struct LayerArgs {
+  int T, d, n, E;
+  int64_t slot_cap, tile_cap;
+  bool f32;  // element type: fp32 when true, bf16 otherwise
+  // routing
+  const int32_t *expert_offsets, *expert_order, *slot_token, *token_offsets, *token_slots;
+  const int32_t *tile_expert, *tile_row, *totals;
+  const float* slot_weight;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr);
+
+// Forward: K1 up-proj + SwiGLU, K2 down-proj, K3 aggregation.
+hipError_t launch_up_swiglu(const LayerArgs& a, const void* X, const void* W1, void* H,
+                            void* Aact, hipStream_t st);
+hipError_t launch_down(const LayerArgs& a, const void* Aact, const void* W2, void* Y,
+                       hipStream_t st);
+// out[t] = sum over t's slots of (weighted ? s : 1) * rows[slot]
+hipError_t launch_aggregate(const LayerArgs& a, const void* rows, bool weighted, void* out,
+                            int width, hipStream_t st);
+
+// Backward: K4 dH (+dS, dSwiGLU, s*A), K5 dX-tilde, K7 dW1, K8 dW2.
+hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const void* H,
+                     void* dH, void* As, float* dS, hipStream_t st);
+hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
+                      hipStream_t st);
+hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1,
+                      hipStream_t st);
+hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2,
+                      hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,228 @@
+// C ABI of the MoE layer library: argument validation, workspace sizing and
+// the launch sequence of each entry point.  Validation and sizing run on the
+// host only and touch no HIP API, so a bad call enqueues nothing.
+#include "moe.h"
+
+#include <limits.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace {
+
+using moe::cdiv;
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t elem_size(const moe_problem* p) { return p->dtype == MOE_F32 ? 4 : 2; }
+
+int check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID;
+  if (p->T < 1 || p->d < 1 || p->n < 1 || p->E < 1 || p->K < 1 || p->M_tile < 1)
+    return MOE_ERR_INVALID;
+  if (p->K > p->E) return MOE_ERR_INVALID;
+  if (p->dtype != MOE_BF16 && p->dtype != MOE_F32) return MOE_ERR_INVALID;
+  if (p->mode != MOE_ROUTE_TC && p->mode != MOE_ROUTE_TR) return MOE_ERR_INVALID;
+  if (p->K > 32 || p->E > 1024 || p->M_tile > 1024) return MOE_ERR_UNSUPPORTED;
+  if (p->d % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (p->n != 64 && p->n != 128 && p->n != 256 && p->n != 384) return MOE_ERR_UNSUPPORTED;
+  // Kernels index rows with 32-bit element offsets.
+  const int64_t slot_cap = p->T * p->K + p->E * p->M_tile;
+  if (p->T > INT_MAX / 64 || p->E > INT_MAX / p->T) return MOE_ERR_UNSUPPORTED;
+  if (p->T * p->d >= INT_MAX || slot_cap * 2 * p->n >= INT_MAX || slot_cap * p->d >= INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+void sizes_of(const moe_problem* p, moe_sizes_t* s) {
+  const int64_t es = elem_size(p);
+  s->slot_cap = p->T * p->K + p->E * p->M_tile;
+  s->tile_cap = cdiv<int64_t>(s->slot_cap, moe::kTileM) + p->E;
+  s->ws_route = moe::RouteWs::make(p->T, p->E).total;
+  // forward transients: A [slot_cap, n], Y [slot_cap, d]
+  s->ws_fwd = align256(size_t(s->slot_cap * p->n * es)) + align256(size_t(s->slot_cap * p->d * es));
+  // backward transients: dH [slot_cap, 2n], s*A [slot_cap, n], dX~ [slot_cap, d]
+  s->ws_bwd = align256(size_t(s->slot_cap * 2 * p->n * es)) +
+              align256(size_t(s->slot_cap * p->n * es)) +
+              align256(size_t(s->slot_cap * p->d * es));
+}
+
+bool routing_ok(const moe_routing* r) {
+  return r && aligned16(r->tc_counts) && aligned16(r->counts) && aligned16(r->expert_offsets) &&
+         aligned16(r->expert_order) && aligned16(r->topk_ids) && aligned16(r->slot_token) &&
+         aligned16(r->slot_weight) && aligned16(r->token_offsets) && aligned16(r->token_slots) &&
+         aligned16(r->tile_expert) && aligned16(r->tile_row) && aligned16(r->totals);
+}
+
+// A trace must name real events: a NULL handle would make hipEventRecord
+// fail and leave an error behind for the next launch check.
+bool trace_ok(const moe_trace* t) {
+  if (!t || !t->events || t->count <= 0) return true;
+  for (int i = 0; i < t->count; ++i)
+    if (!t->events[i]) return false;
+  return true;
+}
+
+moe::TraceHook hook(const moe_trace* t) {
+  moe::TraceHook h;
+  if (t && t->events && t->count > 0) {
+    h.events = t->events;
+    h.count = t->count;
+  }
+  return h;
+}
+
+moe::LayerArgs layer_args(const moe_problem* p, const moe_routing* r) {
+  moe_sizes_t s;
+  sizes_of(p, &s);
+  moe::LayerArgs a;
+  a.T = int(p->T);
+  a.d = int(p->d);
+  a.n = int(p->n);
+  a.E = int(p->E);
+  a.slot_cap = s.slot_cap;
+  a.tile_cap = s.tile_cap;
+  a.f32 = p->dtype == MOE_F32;
+  a.expert_offsets = r->expert_offsets;
+  a.expert_order = r->expert_order;
+  a.slot_token = r->slot_token;
+  a.token_offsets = r->token_offsets;
+  a.token_slots = r->token_slots;
+  a.tile_expert = r->tile_expert;
+  a.tile_row = r->tile_row;
+  a.totals = r->totals;
+  a.slot_weight = r->slot_weight;
+  return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported problem";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_sizes(const moe_problem* p, moe_sizes_t* out) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID;
+  sizes_of(p, out);
+  return MOE_OK;
+}
+
+int moe_route(const moe_problem* p, const float* logits, const moe_routing* r, void* ws,
+              size_t ws_bytes, void* stream, const moe_trace* trace) {
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(logits) || !routing_ok(r) || !aligned16(ws) || !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  moe_sizes_t s;
+  sizes_of(p, &s);
+  if (ws_bytes < s.ws_route) return MOE_ERR_WORKSPACE;
+  moe::RouteArgs a;
+  a.T = int(p->T);
+  a.E = int(p->E);
+  a.K = int(p->K);
+  a.M = int(p->M_tile);
+  a.mode = p->mode;
+  a.logits = logits;
+  a.tc_counts = r->tc_counts;
+  a.counts = r->counts;
+  a.expert_offsets = r->expert_offsets;
+  a.expert_order = r->expert_order;
+  a.topk_ids = r->topk_ids;
+  a.slot_token = r->slot_token;
+  a.slot_weight = r->slot_weight;
+  a.token_offsets = r->token_offsets;
+  a.token_slots = r->token_slots;
+  a.tile_expert = r->tile_expert;
+  a.tile_row = r->tile_row;
+  a.totals = r->totals;
+  a.ws = ws;
+  return hip_status(moe::launch_route(a, static_cast<hipStream_t>(stream), hook(trace)));
+}
+
+int moe_fwd(const moe_problem* p, const void* X, const void* W1, const void* W2,
+            const moe_routing* r, void* O, void* H, void* ws, size_t ws_bytes, void* stream,
+            const moe_trace* trace) {
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !routing_ok(r) || !aligned16(O) ||
+      !aligned16(H) || !aligned16(ws) || !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  moe_sizes_t s;
+  sizes_of(p, &s);
+  if (ws_bytes < s.ws_fwd) return MOE_ERR_WORKSPACE;
+  const moe::LayerArgs a = layer_args(p, r);
+  const moe::TraceHook tr = hook(trace);
+  hipStream_t sm = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  void* Aact = w;
+  void* Y = w + align256(size_t(s.slot_cap * p->n * elem_size(p)));
+
+  tr.mark(sm, 0);
+  hipError_t e = moe::launch_up_swiglu(a, X, W1, H, Aact, sm);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  tr.mark(sm, 1);
+  e = moe::launch_down(a, Aact, W2, Y, sm);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  tr.mark(sm, 2);
+  e = moe::launch_aggregate(a, Y, true, O, a.d, sm);
+  tr.mark(sm, 3);
+  return hip_status(e);
+}
+
+int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, const void* W1,
+            const void* W2, const moe_routing* r, void* dX, void* dW1, void* dW2, float* dS,
+            void* ws, size_t ws_bytes, void* stream, const moe_trace* trace) {
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(dO) || !aligned16(X) || !aligned16(H) || !aligned16(W1) || !aligned16(W2) ||
+      !routing_ok(r) || !aligned16(dX) || !aligned16(dW1) || !aligned16(dW2) || !aligned16(dS) ||
+      !aligned16(ws) || !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  moe_sizes_t s;
+  sizes_of(p, &s);
+  if (ws_bytes < s.ws_bwd) return MOE_ERR_WORKSPACE;
+  const moe::LayerArgs a = layer_args(p, r);
+  const moe::TraceHook tr = hook(trace);
+  hipStream_t sm = static_cast<hipStream_t>(stream);
+  const int64_t es = elem_size(p);
+  char* w = static_cast<char*>(ws);
+  void* dH = w;
+  void* As = w + align256(size_t(s.slot_cap * 2 * p->n * es));
+  void* dXt = static_cast<char*>(As) + align256(size_t(s.slot_cap * p->n * es));
+
+  tr.mark(sm, 0);
+  hipError_t e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  tr.mark(sm, 1);
+  e = moe::launch_dxt(a, dH, W1, dXt, sm);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  tr.mark(sm, 2);
+  e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  tr.mark(sm, 3);
+  e = moe::launch_dw1(a, X, dH, dW1, sm);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  tr.mark(sm, 4);
+  e = moe::launch_dw2(a, As, dO, dW2, sm);
+  tr.mark(sm, 5);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+"""Python binding of libmoe.so (ctypes).  Argument marshalling only: every
+step of routing, forward and backward runs in the library's HIP kernels;
+torch provides device memory and the stream.
+
+If the library is missing this module raises instead of computing anything
+another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_BF16, MOE_F32 = 0, 1
+MOE_ROUTE_TC, MOE_ROUTE_TR = 0, 1
+TILE_M = 128
+
+ROUTE_KERNELS = ("route_clear", "route_topk", "route_round", "route_select", "route_tscan",
+                 "route_tslots")
+FWD_KERNELS = ("up_swiglu", "down", "aggregate_O")
+BWD_KERNELS = ("dh", "dxt", "aggregate_dX", "dw1", "dw2")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("n", ctypes.c_int64),
+                ("E", ctypes.c_int64), ("K", ctypes.c_int64), ("M_tile", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32)]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("slot_cap", ctypes.c_int64), ("tile_cap", ctypes.c_int64),
+                ("ws_route", ctypes.c_size_t), ("ws_fwd", ctypes.c_size_t),
+                ("ws_bwd", ctypes.c_size_t)]
+
+
+ROUTING_FIELDS = ("tc_counts", "counts", "expert_offsets", "expert_order", "topk_ids",
+                  "slot_token", "slot_weight", "token_offsets", "token_slots", "tile_expert",
+                  "tile_row", "totals")
+
+
+class RoutingStruct(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in ROUTING_FIELDS]
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("count", ctypes.c_int32)]
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """Loads libmoe.so (built in-tree by fine_grained_mixture_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoEError(f"{LIB_PATH} is missing; build it with "
+                       "`python -m fine_grained_mixture_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, V, S = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
+    L.moe_sizes.argtypes = [P(Problem), P(Sizes)]
+    L.moe_route.argtypes = [P(Problem), V, P(RoutingStruct), V, S, V, P(Trace)]
+    L.moe_fwd.argtypes = [P(Problem), V, V, V, P(RoutingStruct), V, V, V, S, V, P(Trace)]
+    L.moe_bwd.argtypes = [P(Problem), V, V, V, V, V, P(RoutingStruct), V, V, V, V, V, S, V,
+                          P(Trace)]
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    for f in ("moe_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_abi_version"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        msg = lib().moe_status_string(status).decode()
+        raise MoEError(f"libmoe returned {status}: {msg}")
+
+
+def problem(T, d, n, E, K, M_tile, dtype=torch.bfloat16, mode="tr") -> Problem:
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[dtype]
+    md = {"tc": MOE_ROUTE_TC, "tr": MOE_ROUTE_TR}[mode]
+    return Problem(T, d, n, E, K, M_tile, dt, md)
+
+
+def torch_dtype(p: Problem):
+    return torch.float32 if p.dtype == MOE_F32 else torch.bfloat16
+
+
+def sizes(p: Problem) -> Sizes:
+    s = Sizes()
+    _check(lib().moe_sizes(ctypes.byref(p), ctypes.byref(s)))
+    return s
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _trace(events):
+    if not events:
+        return None
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    return Trace(arr, len(events))
+
+
+def _dev(t: torch.Tensor, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoEError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MoEError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoEError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoEError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Routing:
+    """Device-resident routing metadata (see moe_routing in include/moe.h)."""
+    problem: Problem
+    tensors: dict
+    struct: RoutingStruct = field(repr=False)
+
+    def __getattr__(self, k):
+        t = self.__dict__.get("tensors")
+        if t is not None and k in t:
+            return t[k]
+        raise AttributeError(k)
+
+    @property
+    def S(self) -> int:
+        """Slot count (copies one int from the device)."""
+        return int(self.tensors["totals"][0].item())
+
+
+def alloc_routing(p: Problem, device="cuda") -> Routing:
+    s = sizes(p)
+    i32 = dict(dtype=torch.int32, device=device)
+    T, E, K = p.T, p.E, p.K
+    t = {
+        "tc_counts": torch.empty(E, **i32),
+        "counts": torch.empty(E, **i32),
+        "expert_offsets": torch.empty(E + 1, **i32),
+        "expert_order": torch.empty(E, **i32),
+        "topk_ids": torch.empty(T * K, **i32),
+        "slot_token": torch.empty(s.slot_cap, **i32),
+        "slot_weight": torch.empty(s.slot_cap, dtype=torch.float32, device=device),
+        "token_offsets": torch.empty(T + 1, **i32),
+        "token_slots": torch.empty(s.slot_cap, **i32),
+        "tile_expert": torch.empty(s.tile_cap, **i32),
+        "tile_row": torch.empty(s.tile_cap, **i32),
+        "totals": torch.empty(2, **i32),
+    }
+    st = RoutingStruct(*[t[f].data_ptr() for f in ROUTING_FIELDS])
+    return Routing(p, t, st)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def route(p: Problem, logits: torch.Tensor, rt: Routing | None = None, ws=None, stream=None,
+          events=None) -> Routing:
+    """moe_route: top-K token choice, optionally token rounding."""
+    lg = _dev(logits, "logits", torch.float32, (p.T, p.E))
+    rt = rt if rt is not None else alloc_routing(p, logits.device)
+    ws = ws if ws is not None else workspace(sizes(p).ws_route, logits.device)
+    tr = _trace(events)
+    _check(lib().moe_route(ctypes.byref(p), lg, ctypes.byref(rt.struct),
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
+                           ctypes.byref(tr) if tr else None))
+    return rt
+
+
+def forward(p: Problem, X, W1, W2, rt: Routing, out=None, ws=None, stream=None, events=None):
+    """moe_fwd: returns O [T, d] and H [slot_cap, 2n] (rows [0, S) valid)."""
+    dt = torch_dtype(p)
+    s = sizes(p)
+    dev = X.device
+    x = _dev(X, "X", dt, (p.T, p.d))
+    w1 = _dev(W1, "W1", dt, (p.E, p.d, 2 * p.n))
+    w2 = _dev(W2, "W2", dt, (p.E, p.n, p.d))
+    O, H = out if out is not None else (torch.empty(p.T, p.d, dtype=dt, device=dev),
+                                        torch.empty(s.slot_cap, 2 * p.n, dtype=dt, device=dev))
+    ws = ws if ws is not None else workspace(s.ws_fwd, dev)
+    tr = _trace(events)
+    _check(lib().moe_fwd(ctypes.byref(p), x, w1, w2, ctypes.byref(rt.struct),
+                         _dev(O, "O", dt, (p.T, p.d)), _dev(H, "H", dt, (s.slot_cap, 2 * p.n)),
+                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
+                         ctypes.byref(tr) if tr else None))
+    return O, H
+
+
+def backward(p: Problem, dO, X, H, W1, W2, rt: Routing, out=None, ws=None, stream=None,
+             events=None):
+    """moe_bwd: returns dX [T, d], dW1 [E, d, 2n], dW2 [E, n, d], dS [slot_cap]."""
+    dt = torch_dtype(p)
+    s = sizes(p)
+    dev = X.device
+    if out is None:
+        out = (torch.empty(p.T, p.d, dtype=dt, device=dev),
+               torch.empty(p.E, p.d, 2 * p.n, dtype=dt, device=dev),
+               torch.empty(p.E, p.n, p.d, dtype=dt, device=dev),
+               torch.empty(s.slot_cap, dtype=torch.float32, device=dev))
+    dX, dW1, dW2, dS = out
+    ws = ws if ws is not None else workspace(s.ws_bwd, dev)
+    tr = _trace(events)
+    _check(lib().moe_bwd(ctypes.byref(p), _dev(dO, "dO", dt, (p.T, p.d)),
+                         _dev(X, "X", dt, (p.T, p.d)), _dev(H, "H", dt, (s.slot_cap, 2 * p.n)),
+                         _dev(W1, "W1", dt, (p.E, p.d, 2 * p.n)),
+                         _dev(W2, "W2", dt, (p.E, p.n, p.d)), ctypes.byref(rt.struct),
+                         _dev(dX, "dX", dt, (p.T, p.d)),
+                         _dev(dW1, "dW1", dt, (p.E, p.d, 2 * p.n)),
+                         _dev(dW2, "dW2", dt, (p.E, p.n, p.d)),
+                         _dev(dS, "dS", torch.float32, (s.slot_cap,)),
+                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
+                         ctypes.byref(tr) if tr else None))
+    return dX, dW1, dW2, dS
+
+
+class MoELayerFunction(torch.autograd.Function):
+    """Autograd wrapper.  Saves exactly X and H (plus the routing metadata) for
+    the backward; the router-facing gradient dS is left on the routing object
+    (``routing.dS``) because the router itself sits outside this layer."""
+
+    @staticmethod
+    def forward(ctx, X, W1, W2, logits, K, M_tile, mode):
+        T, d = X.shape
+        E, _, n2 = W1.shape
+        p = problem(T, d, n2 // 2, E, K, M_tile, X.dtype, mode)
+        rt = route(p, logits)
+        O, H = forward(p, X, W1, W2, rt)
+        ctx.save_for_backward(X, H, W1, W2)
+        ctx.moe = (p, rt)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        X, H, W1, W2 = ctx.saved_tensors
+        p, rt = ctx.moe
+        dX, dW1, dW2, dS = backward(p, dO.contiguous(), X, H, W1, W2, rt)
+        rt.tensors["dS"] = dS
+        return dX, dW1, dW2, None, None, None, None
+
+
+def moe_layer(X, W1, W2, logits, K, M_tile, mode="tr"):
+    return MoELayerFunction.apply(X, W1, W2, logits, K, M_tile, mode)

@@ -1,0 +1,186 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fine-grained MoE layer library.
+ *
+ * The library computes one fine-grained Mixture-of-Experts layer as described
+ * in "SonicMoE: Accelerating MoE with IO and Tile-aware Optimizations"
+ * (ICLR-2026 notes on papernotes.org; arXiv abstract on mlsanity.com):
+ *
+ *   moe_route  top-K token-choice routing on softmax router scores, then
+ *              optionally token rounding of every expert's token count to a
+ *              multiple of M_tile (notes, key design 1);
+ *   moe_fwd    up-projection with the token gather fused into the operand
+ *              load and SwiGLU in the epilogue, down-projection, and the
+ *              router-weighted aggregation (notes, method > overall
+ *              framework, and key design 2);
+ *   moe_bwd    the minimal-activation backward: it reads only X, H and the
+ *              routing metadata, computes dH and dS = <dA', A> in the
+ *              epilogue of the dH grouped GEMM, and forms dW1 / dW2 with
+ *              varlen-K grouped GEMMs (notes, key designs 2 and 3).
+ *
+ * Problem statement (notes, background and key design 3): T tokens, model
+ * dim d, expert intermediate dim n, E experts, K experts per token, and the
+ * GEMM M tile M_tile that token rounding aligns counts to.
+ *   X  [T, d]         W1 [E, d, 2n]  (columns [0, n) gate, [n, 2n) up)
+ *   W2 [E, n, d]      O  [T, d]       H  [slot_cap, 2n]  (pre-activation)
+ * All matrices are dense, row-major, with no padding between rows.
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers, allocated and owned by the
+ *     caller.  The library never allocates or frees memory and keeps no
+ *     device state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No call synchronises the host or copies device data to
+ *     the host.  Data-dependent sizes (slot count S, tile count) stay on the
+ *     device in `moe_routing.totals`; kernels past them exit early.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     failure the call returns a negative moe_status and enqueues nothing.
+ *     A HIP launch failure returns MOE_ERR_HIP.
+ *   - Pointers must be 16-byte aligned.
+ *   - Floating-point inputs and outputs use `dtype` (bf16 or fp32); logits,
+ *     gate weights and dS are always fp32; accumulation is always fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Rows per M tile of the grouped GEMMs; the tile schedule in moe_routing is
+ * expressed in these units. */
+#define MOE_GEMM_TILE_M 128
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,     /* null / misaligned pointer, bad dimension     */
+  MOE_ERR_UNSUPPORTED = -2, /* valid problem this build does not handle     */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_sizes reports     */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed   */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_ROUTE_TC = 0, /* vanilla top-K token choice                            */
+  MOE_ROUTE_TR = 1  /* token choice followed by token rounding to M_tile     */
+} moe_route_mode;
+
+typedef struct {
+  int64_t T, d, n, E, K, M_tile;
+  int32_t dtype; /* moe_dtype      */
+  int32_t mode;  /* moe_route_mode */
+} moe_problem;
+
+typedef struct {
+  int64_t slot_cap; /* upper bound on slots S: T*K + E*M_tile                  */
+  int64_t tile_cap; /* upper bound on M tiles: ceil(slot_cap/TILE_M) + E       */
+  size_t ws_route;  /* workspace bytes moe_route needs                         */
+  size_t ws_fwd;    /* workspace bytes moe_fwd needs                           */
+  size_t ws_bwd;    /* workspace bytes moe_bwd needs                           */
+} moe_sizes_t;
+
+/*
+ * Routing metadata (the "routing metadata" the notes' key design 3 keeps
+ * for the backward).  Every array is a caller-allocated device buffer.
+ * Slots are in canonical order: experts ascending, and tokens ascending
+ * inside an expert.  moe_route writes all of it; moe_fwd / moe_bwd read it.
+ */
+typedef struct {
+  int32_t *tc_counts;      /* [E]        f_e, token-choice count per expert  */
+  int32_t *counts;         /* [E]        r_e, final count (r_e = f_e for TC)  */
+  int32_t *expert_offsets; /* [E+1]      exclusive scan of counts             */
+  int32_t *expert_order;   /* [E]        experts by descending r_e (ties: e)  */
+  int32_t *topk_ids;       /* [T*K]      token-choice experts, best first     */
+  int32_t *slot_token;     /* [slot_cap] token of each slot                   */
+  float *slot_weight;      /* [slot_cap] gate weight s = softmax prob p[t,e]  */
+  int32_t *token_offsets;  /* [T+1]      CSR offsets of each token's slots    */
+  int32_t *token_slots;    /* [slot_cap] a token's slots, ascending expert    */
+  int32_t *tile_expert;    /* [tile_cap] expert of each M tile                */
+  int32_t *tile_row;       /* [tile_cap] first slot row of each M tile        */
+  int32_t *totals;         /* [2]        S, number of M tiles                 */
+} moe_routing;
+
+/*
+ * Optional per-kernel timing.  When `trace` is non-NULL and trace->count is
+ * at least the number of kernels the call launches plus one, the call
+ * records trace->events[i] (hipEvent_t, created by the caller) on `stream`
+ * before its i-th kernel and trace->events[kernels] after the last one.
+ * moe_route launches 6 kernels, moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
+ * dX aggregate, dW1, dW2).  NULL disables tracing.
+ */
+typedef struct {
+  void **events;
+  int32_t count;
+} moe_trace;
+
+/* Host only; touches no device.  Validates `p` and fills `out`.
+ * Errors: MOE_ERR_INVALID for null arguments or T, d, n, E, K, M_tile < 1,
+ * K > E, unknown dtype/mode; MOE_ERR_UNSUPPORTED for K > 32, E > 1024,
+ * d % 64 != 0, n not in {64, 128, 256, 384, 512}, M_tile > 1024, or sizes
+ * whose slot or element counts overflow 32-bit indexing. */
+int moe_sizes(const moe_problem *p, moe_sizes_t *out);
+
+/*
+ * Routing (notes, key design 1).  logits: [T, E] fp32 device buffer.
+ *   p[t,e]  = softmax over the E logits of token t, evaluated in fp64;
+ *   TopK(t) = the K largest fp32 logits, equal logits to the lower expert;
+ *   f_e     = number of tokens whose TopK holds e;
+ *   TC:  r_e = f_e and expert e keeps exactly those tokens;
+ *   TR:  lo/hi = the multiples of M_tile just below/above f_e; r_e = hi when
+ *        hi - f_e < f_e - lo and hi <= T, else lo; expert e keeps the first
+ *        r_e tokens ordered by (e in TopK(t), p[t,e]) descending, equal keys
+ *        to the lower token;
+ *   s = p[t,e] for every kept pair (no renormalisation).
+ * ws: at least sizes.ws_route bytes.  Writes every field of `r`.
+ */
+int moe_route(const moe_problem *p, const float *logits, const moe_routing *r,
+              void *ws, size_t ws_bytes, void *stream, const moe_trace *trace);
+
+/*
+ * Forward (notes, method > overall framework; key design 2).  For every
+ * expert e with kept tokens I_e:
+ *   H_e = X[I_e] W1_e          (rows gathered inside the GEMM operand load)
+ *   A_e = SiLU(H_e[:, :n]) * H_e[:, n:]   (epilogue, from H rounded to dtype)
+ *   Y_e = A_e W2_e
+ *   O[t] = sum over t's slots of s * Y   (a token without slots gets 0)
+ * Outputs: O [T, d]; H [slot_cap, 2n], rows [0, S) valid, saved for moe_bwd.
+ * ws: at least sizes.ws_fwd bytes (holds the transient A and Y).
+ */
+int moe_fwd(const moe_problem *p, const void *X, const void *W1,
+            const void *W2, const moe_routing *r, void *O, void *H, void *ws,
+            size_t ws_bytes, void *stream, const moe_trace *trace);
+
+/*
+ * Minimal-activation backward (notes, key designs 2 and 3).  Reads only
+ * dO, X, H, W1, W2 and the routing; never Y or a gathered copy of X.
+ *   dA'_e = dO[I_e] W2_e^T, A recomputed from H,
+ *   dS    = rowsum(dA' * A)          (per slot, fp32, not scaled by s)
+ *   dA    = s * dA',  dH = [dA * u * sig(g) * (1 + g (1 - sig(g))),
+ *                           dA * SiLU(g)]  with g, u the halves of H
+ *   dX[t] = sum over t's slots of dH W1_e^T
+ *   dW1_e = X[I_e]^T dH_e,   dW2_e = (s * A_e)^T dO[I_e]   (varlen-K)
+ * Outputs: dX [T, d], dW1 [E, d, 2n], dW2 [E, n, d] (experts without slots
+ * get zeros), dS [slot_cap] fp32 with rows [0, S) valid.
+ * ws: at least sizes.ws_bwd bytes.
+ */
+int moe_bwd(const moe_problem *p, const void *dO, const void *X, const void *H,
+            const void *W1, const void *W2, const moe_routing *r, void *dX,
+            void *dW1, void *dW2, float *dS, void *ws, size_t ws_bytes,
+            void *stream, const moe_trace *trace);
+
+/* Static, NUL-terminated description of a moe_status value. */
+const char *moe_status_string(int status);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

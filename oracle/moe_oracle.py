@@ -292,66 +292,89 @@ def backward_naive(dO, X, W1, W2, rt: Routing, cache):
 
 
 # --------------------------------------------------------------------------
-# Sampled evaluation for full-size shapes (same arithmetic, restricted rows)
+# Sampled evaluation for full-size shapes (same arithmetic, restricted rows).
+# These recompute H from X and W1 themselves and convert only the rows and
+# experts they touch to fp64, so they also serve shapes whose full fp64 copy
+# would not fit in memory.
 # --------------------------------------------------------------------------
+
+def _slot_terms(slots, X, W1, W2, dO, rt: Routing):
+    """For a batch of slots of ONE expert: H, A, dA', dS and dH."""
+    e = int(rt.slot_expert[slots[0]])
+    tok = rt.slot_token[slots]
+    W1e, W2e = _f64(W1[e]), _f64(W2[e])
+    n = W2e.shape[0]
+    H = _f64(X[tok]) @ W1e
+    A = swiglu(H, n)
+    dAp = _f64(dO[tok]) @ W2e.T
+    g, u = H[:, :n], H[:, n:]
+    s = rt.slot_weight[slots, None]
+    dA = s * dAp
+    sg = sigmoid(g)
+    dH = np.concatenate([dA * u * sg * (1.0 + g * (1.0 - sg)), dA * silu(g)], axis=1)
+    return H, A, (dAp * A).sum(axis=1), dH
+
+
+def _by_expert(slots, rt: Routing):
+    slots = np.asarray(slots, dtype=np.int64)
+    ex = rt.slot_expert[slots]
+    for e in np.unique(ex):
+        idx = np.nonzero(ex == e)[0]
+        yield idx, slots[idx]
+
 
 def forward_tokens(tokens, X, W1, W2, rt: Routing):
     """O[t] for selected tokens only, from each token's own slots."""
-    X, W1, W2 = _f64(X), _f64(W1), _f64(W2)
-    n = W1.shape[2] // 2
     out = np.zeros((len(tokens), X.shape[1]))
-    for i, t in enumerate(tokens):
-        for j in range(rt.token_offsets[t], rt.token_offsets[t + 1]):
-            p = rt.token_slots[j]
-            e = rt.slot_expert[p]
-            h = X[t] @ W1[e]
-            out[i] += rt.slot_weight[p] * (swiglu(h[None], n)[0] @ W2[e])
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    slots = np.concatenate([rt.token_slots[rt.token_offsets[t]:rt.token_offsets[t + 1]]
+                            for t in tokens] + [np.zeros(0, np.int64)])
+    for _, sl in _by_expert(slots, rt):
+        e = int(rt.slot_expert[sl[0]])
+        A = swiglu(_f64(X[rt.slot_token[sl]]) @ _f64(W1[e]), W2.shape[1])
+        Y = A @ _f64(W2[e])
+        for k, p in enumerate(sl):
+            out[pos[int(rt.slot_token[p])]] += rt.slot_weight[p] * Y[k]
     return out
 
 
-def slot_grads(slots, dO, H, W2, rt: Routing):
-    """dS and dH for selected slots (same formulas as backward_minimal)."""
-    dO, H, W2 = _f64(dO), _f64(H), _f64(W2)
+def slot_grads(slots, X, W1, W2, dO, rt: Routing):
+    """dS and dH for selected slots (the formulas of backward_minimal)."""
+    slots = np.asarray(slots, dtype=np.int64)
     n = W2.shape[1]
     dS = np.zeros(len(slots))
     dH = np.zeros((len(slots), 2 * n))
-    for i, p in enumerate(slots):
-        t, e = rt.slot_token[p], rt.slot_expert[p]
-        dap = dO[t] @ W2[e].T
-        g, u = H[p, :n], H[p, n:]
-        dS[i] = np.dot(dap, silu(g) * u)
-        da = rt.slot_weight[p] * dap
-        sg = sigmoid(g)
-        dH[i] = np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)),
-                                da * silu(g)])
+    for idx, sl in _by_expert(slots, rt):
+        _, _, dS[idx], dH[idx] = _slot_terms(sl, X, W1, W2, dO, rt)
     return dS, dH
 
 
-def dx_tokens(tokens, dO, H, W1, W2, rt: Routing):
+def dx_tokens(tokens, X, W1, W2, dO, rt: Routing):
     """dX[t] for selected tokens: sum over t's slots of dH W1_e^T."""
-    W1 = _f64(W1)
-    out = np.zeros((len(tokens), W1.shape[1]))
-    for i, t in enumerate(tokens):
-        slots = rt.token_slots[rt.token_offsets[t]:rt.token_offsets[t + 1]]
-        if len(slots) == 0:
-            continue
-        _, dH = slot_grads(slots, dO, H, W2, rt)
-        for k, p in enumerate(slots):
-            out[i] += dH[k] @ W1[rt.slot_expert[p]].T
+    out = np.zeros((len(tokens), X.shape[1]))
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    slots = np.concatenate([rt.token_slots[rt.token_offsets[t]:rt.token_offsets[t + 1]]
+                            for t in tokens] + [np.zeros(0, np.int64)])
+    for _, sl in _by_expert(slots, rt):
+        e = int(rt.slot_expert[sl[0]])
+        _, _, _, dH = _slot_terms(sl, X, W1, W2, dO, rt)
+        dXt = dH @ _f64(W1[e]).T
+        for k, p in enumerate(sl):
+            out[pos[int(rt.slot_token[p])]] += dXt[k]
     return out
 
 
-def expert_weight_grads(e, dO, X, H, W2, rt: Routing):
+def expert_weight_grads(e, X, W1, W2, dO, rt: Routing):
     """dW1_e and dW2_e for one expert (varlen-K contraction over its slots)."""
-    X, dO, H = _f64(X), _f64(dO), _f64(H)
-    n = H.shape[1] // 2
     a, b = rt.expert_offsets[e], rt.expert_offsets[e + 1]
-    slots = np.arange(a, b)
+    d, n = X.shape[1], W2.shape[1]
+    if a == b:
+        return np.zeros((d, 2 * n)), np.zeros((n, d))
+    sl = np.arange(a, b)
     tok = rt.slot_token[a:b]
-    _, dH = slot_grads(slots, dO, H, W2, rt)
+    _, A, _, dH = _slot_terms(sl, X, W1, W2, dO, rt)
     s = rt.slot_weight[a:b, None]
-    Ae = swiglu(H[a:b], n)
-    return X[tok].T @ dH, (s * Ae).T @ dO[tok]
+    return _f64(X[tok]).T @ dH, (s * A).T @ _f64(dO[tok])
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/moe.h declares, sizes its buffers, and rejects bad arguments on the
+host before anything is enqueued (no GPU needed: no call here reaches a
+launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fine_grained_mixture_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH),
+                                reason="libmoe.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert names == ["moe_abi_version", "moe_bwd", "moe_fwd", "moe_route", "moe_sizes",
+                     "moe_status_string"]
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+
+
+def test_status_strings():
+    L = moe.lib()
+    for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert L.moe_status_string(st)
+    assert L.moe_status_string(7) == b"unknown status"
+
+
+def test_sizes_7b_layer():
+    p = moe.problem(16384, 1536, 256, 128, 8, 128)
+    s = moe.sizes(p)
+    assert s.slot_cap == 16384 * 8 + 128 * 128
+    assert s.tile_cap == -(-s.slot_cap // 128) + 128
+    esz = 2
+    assert s.ws_fwd >= s.slot_cap * (256 + 1536) * esz
+    assert s.ws_bwd >= s.slot_cap * (512 + 256 + 1536) * esz
+    assert s.ws_route >= 16384 * 128 * 8
+
+
+def test_sizes_fp32_doubles_transients():
+    b = moe.sizes(moe.problem(256, 128, 64, 8, 2, 16, dtype=moe.torch.bfloat16))
+    f = moe.sizes(moe.problem(256, 128, 64, 8, 2, 16, dtype=moe.torch.float32))
+    assert f.ws_fwd >= 2 * b.ws_fwd - 512 and f.ws_route == b.ws_route
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("T", 0, INVALID), ("d", -128, INVALID), ("K", 9, INVALID), ("M_tile", 0, INVALID),
+    ("dtype", 5, INVALID), ("mode", 2, INVALID), ("K", 33, UNSUPPORTED),
+    ("d", 192, UNSUPPORTED), ("n", 96, UNSUPPORTED), ("n", 512, UNSUPPORTED),
+    ("E", 2048, UNSUPPORTED), ("M_tile", 4096, UNSUPPORTED), ("T", 1 << 26, UNSUPPORTED),
+])
+def test_invalid_problems(field, value, status):
+    p = moe.problem(256, 128, 64, 8, 2, 16)
+    if field == "K" and value == 33:
+        p.E = 64
+    setattr(p, field, value)
+    s = moe.Sizes()
+    assert moe.lib().moe_sizes(ctypes.byref(p), ctypes.byref(s)) == status
+
+
+def _routing(ptr=FAKE):
+    return moe.RoutingStruct(*([ptr] * len(moe.ROUTING_FIELDS)))
+
+
+def test_route_validation_before_launch():
+    L = moe.lib()
+    p = moe.problem(256, 128, 64, 8, 2, 16)
+    need = moe.sizes(p).ws_route
+    r = _routing()
+    assert L.moe_route(ctypes.byref(p), None, ctypes.byref(r), FAKE, need, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(p), FAKE + 4, ctypes.byref(r), FAKE, need, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(p), FAKE, ctypes.byref(_routing(0)), FAKE, need, None,
+                       None) == INVALID
+    assert L.moe_route(ctypes.byref(p), FAKE, ctypes.byref(r), FAKE, need - 1, None,
+                       None) == WORKSPACE
+    assert L.moe_route(None, FAKE, ctypes.byref(r), FAKE, need, None, None) == INVALID
+
+
+def test_fwd_bwd_validation_before_launch():
+    L = moe.lib()
+    p = moe.problem(256, 128, 64, 8, 2, 16)
+    s = moe.sizes(p)
+    r = _routing()
+    args = [FAKE] * 3
+    assert L.moe_fwd(ctypes.byref(p), *args, ctypes.byref(r), FAKE, FAKE, FAKE, s.ws_fwd - 1,
+                     None, None) == WORKSPACE
+    assert L.moe_fwd(ctypes.byref(p), None, FAKE, FAKE, ctypes.byref(r), FAKE, FAKE, FAKE,
+                     s.ws_fwd, None, None) == INVALID
+    assert L.moe_bwd(ctypes.byref(p), *([FAKE] * 5), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE,
+                     FAKE, s.ws_bwd - 1, None, None) == WORKSPACE
+    assert L.moe_bwd(ctypes.byref(p), *([FAKE] * 5), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE + 8,
+                     FAKE, s.ws_bwd, None, None) == INVALID
+    bad = moe.problem(256, 128, 64, 8, 2, 16)
+    bad.n = 100
+    assert L.moe_bwd(ctypes.byref(bad), *([FAKE] * 5), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE,
+                     FAKE, s.ws_bwd, None, None) == UNSUPPORTED
+
+
+def test_null_trace_event_rejected():
+    L = moe.lib()
+    p = moe.problem(256, 128, 64, 8, 2, 16)
+    need = moe.sizes(p).ws_route
+    ev = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
+    tr = moe.Trace(ev, 7)
+    assert L.moe_route(ctypes.byref(p), FAKE, ctypes.byref(_routing()), FAKE, need, None,
+                       ctypes.byref(tr)) == INVALID

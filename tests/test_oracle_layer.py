@@ -156,11 +156,11 @@ def test_sampled_helpers_match_full():
     dX, dW1, dW2, dS = orc.backward_minimal(dO, X, c["H"], W1, W2, rt)
     toks = [0, 3, 17, 49]
     np.testing.assert_allclose(orc.forward_tokens(toks, X, W1, W2, rt), O[toks], rtol=1e-13, atol=1e-14)
-    np.testing.assert_allclose(orc.dx_tokens(toks, dO, c["H"], W1, W2, rt), dX[toks], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(orc.dx_tokens(toks, X, W1, W2, dO, rt), dX[toks], rtol=1e-13, atol=1e-14)
     slots = [0, 5, rt.S - 1]
-    np.testing.assert_allclose(orc.slot_grads(slots, dO, c["H"], W2, rt)[0], dS[slots], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(orc.slot_grads(slots, X, W1, W2, dO, rt)[0], dS[slots], rtol=1e-13, atol=1e-14)
     for e in range(5):
-        g1, g2 = orc.expert_weight_grads(e, dO, X, c["H"], W2, rt)
+        g1, g2 = orc.expert_weight_grads(e, X, W1, W2, dO, rt)
         np.testing.assert_allclose(g1, dW1[e], rtol=1e-13, atol=1e-14)
         np.testing.assert_allclose(g2, dW2[e], rtol=1e-13, atol=1e-14)
 
