@@ -1,53 +1,71 @@
-// Building blocks of the grouped GEMMs on gfx950: LDS tiles, operand loaders
-// with the token gather fused into the global->LDS copy, and a
-// double-buffered bf16/fp32 MFMA main loop.
+// Building blocks of the grouped GEMMs on gfx950: LDS tiles filled by
+// direct global->LDS DMA with the token gather done per lane, a multi-stage
+// DMA pipeline, and bf16/fp32 MFMA fragment reads for both operand layouts.
 //
-// Operand convention.  Every GEMM computes C[i][j] = sum_k A[i][k] B[k][j]
-// for one BM x BN output tile.  Both operands are staged in LDS "k-major per
-// row": the A tile as BM rows of BK k-values, the B tile as BN rows (one per
-// output column j) of BK k-values, each row padded by 16 bytes so that the
-// 16-byte fragment reads of 16 consecutive rows hit distinct LDS banks.
+// Operand layouts.  Every GEMM computes C[i][j] = sum_k A[i][k] B[k][j] for
+// one BM x BN output tile, BK = 128 bytes of k per slab (64 bf16 / 32 fp32).
+//   K-major tile   one LDS row of 128 B per output row (i of A, j of B),
+//                  holding that row's BK k-values.  Used where the source
+//                  rows hold k contiguously (X, dO, A, dH, and the weights
+//                  when the contraction runs along their rows).
+//   MN-major tile  one LDS row per k, holding COLS contiguous output
+//                  indices.  Used where the source rows are indexed by k:
+//                  the weights along their columns, and both operands of the
+//                  varlen-K weight-gradient GEMMs (rows = the expert's slots).
 //
-// Loaders:
-//   DirectLoader  source rows already hold k contiguously (X, dO, A, dH,
-//                 and the weights when the contraction runs along their
-//                 rows); each thread copies fixed 8-element octets, with a
-//                 per-row element offset that carries the gather.
-//   TransLoader   source rows are indexed by k (the weights along their
-//                 columns, and both operands of the varlen-K weight-gradient
-//                 GEMMs); each thread reads an 8x8 block (8 k rows x 8
-//                 columns), transposes it in registers and writes 8 LDS rows.
+// DMA.  global_load_lds_dwordx4 copies 16 B per lane and places lane L's
+// bytes at LDS base + 16 L, so one wave instruction fills 1 KB of a tile
+// contiguously while every lane may read any global address (the gather).
+// Tiles are unpadded; bank conflicts are avoided by XOR-swizzling the 16-byte
+// chunks of each row (the lane that fills a physical chunk fetches the
+// logical chunk that belongs there):
+//   K-major:   physical chunk = logical chunk ^ ((row >> 1) & 7)
+//   MN-major:  physical chunk = logical chunk ^ ((k & 3) << 1)
+// so that the 16 rows read by 16 lanes (K-major), or the 4 rows x 32 bytes
+// read by one transposing LDS read (MN-major), fall on distinct banks.
+//
+// Fragment reads.  A 32x32x16 bf16 MFMA takes, in lane l, 8 consecutive
+// k-values of row l % 32 (k half l / 32).  K-major tiles give them with one
+// 16-byte LDS read.  MN-major tiles give them with two ds_read_b64_tr_b16:
+// within each group of 16 lanes, lane s points at (k0 + s/4, c0 + 4 (s%4))
+// and receives the four k-values k0..k0+3 of column c0 + s.
 //
 // The MFMA is issued with the B fragment as its first operand, so each
 // accumulator block holds C^T: lane l owns output row (l % 32) of the block
-// and, for accumulator element r, column (r/4)*8 + (l/32)*4 + r%4.  Four
-// consecutive r therefore address four consecutive columns of one row, which
-// the epilogues store as one vector.
+// and, for accumulator element r, column (r/4)*8 + (l/32)*4 + r%4 — four
+// consecutive r are four consecutive columns of one row.
 #pragma once
 
 #include "common.hpp"
 
 namespace moe {
 
-template <class T_, int BM_, int BN_, int WGM_, int WGN_, bool PAIRED_ = false>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+template <class T_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool PAIRED_ = false>
 struct TileCfg {
   using T = T_;
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr bool PAIRED = PAIRED_;  // B tile = [gate cols | up cols]
+  static constexpr bool PAIRED = PAIRED_;  // B columns = [gate half | up half]
   static constexpr int kThreads = 256;
   static_assert(WGM * WGN == 4, "four waves per workgroup");
-  static constexpr int BK = 128 / int(sizeof(T));     // 128 bytes of k per row
-  static constexpr int LD = BK + 16 / int(sizeof(T));  // padded LDS row (144 B)
+  static constexpr int BK = 128 / int(sizeof(T));  // k-values per slab (128 B)
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int MB = WTM / 32, NB = WTN / 32;
   static_assert(MB >= 1 && NB >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(!PAIRED || NB % 2 == 0, "paired tiles split each wave's columns");
-  static constexpr int OCTS = BK / 8;  // octets per LDS row
   static constexpr int KCH = BK / 16;  // 16-wide k chunks per slab
-  static constexpr int A_ELEMS = BM * LD, B_ELEMS = BN * LD;
-  static constexpr int LDS_ELEMS = 2 * (A_ELEMS + B_ELEMS);
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  // the requested depth, or the deepest that fits in the 160 KB of LDS
+  static constexpr int STAGES =
+      STAGES_ * STAGE_BYTES <= 160 * 1024 ? STAGES_ : (160 * 1024) / STAGE_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
-  // LDS column (B-tile row) of the first column of wave column-block nb.
+  // Tile column (B-tile output index) of the first column of wave block nb.
   __device__ static constexpr int colblock(int wn, int nb) {
     if constexpr (PAIRED) {
       constexpr int half = BN / 2, per = half / WGN, hb = NB / 2;
@@ -58,102 +76,214 @@ struct TileCfg {
   }
 };
 
-// Rows whose k-values are contiguous in memory.  row_off(r) gives the element
-// offset of row r's first k-value from `base`, or -1 for a row that is zero
-// (past the end of the expert).
-template <class Cfg, int ROWS>
-struct DirectLoader {
-  using T = typename Cfg::T;
-  static constexpr int N_OCT = ROWS * Cfg::OCTS;
-  static constexpr int PER = (N_OCT + Cfg::kThreads - 1) / Cfg::kThreads;
-  const T* base;
-  int off[PER];
-  Oct<T> reg[PER];
-
-  template <class RowOff>
-  __device__ __forceinline__ void init(const T* b, RowOff row_off) {
-    base = b;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + i * Cfg::kThreads;
-      const int r = q / Cfg::OCTS, o = q % Cfg::OCTS;
-      int v = -1;
-      if (q < N_OCT) {
-        const int ro = row_off(r);
-        v = ro < 0 ? -1 : ro + o * 8;
-      }
-      off[i] = v;
-    }
-  }
-  __device__ __forceinline__ void load(int k0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (off[i] >= 0) oct_load(reg[i], base + off[i] + k0);
-      else oct_zero(reg[i]);
-    }
-  }
-  __device__ __forceinline__ void store(T* stage) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + i * Cfg::kThreads;
-      if (q < N_OCT) oct_store(stage + (q / Cfg::OCTS) * Cfg::LD + (q % Cfg::OCTS) * 8, reg[i]);
-    }
-  }
-  __device__ __forceinline__ void fetch(int s) { load(s * Cfg::BK); }
-  __device__ __forceinline__ void put(T* stage) const { store(stage); }
-};
-
-// Rows indexed by k.  For slab s, k_off(s, k) gives the element offset of
-// source row k (0 <= k < BK) of that slab from `base`, or -1 for a zero row;
-// col_off(cg) gives the column offset of LDS column group cg (8 columns).
-template <class Cfg, int COLS, class KOff, class ColOff>
-struct TransLoader {
-  using T = typename Cfg::T;
-  static constexpr int KG = Cfg::BK / 8;
-  static constexpr int N_UNITS = (COLS / 8) * KG;
-  static constexpr int PER = (N_UNITS + Cfg::kThreads - 1) / Cfg::kThreads;
-  const T* base;
-  KOff k_off;
-  ColOff col_off;
-  Oct<T> reg[PER][8];
-
-  __device__ __forceinline__ TransLoader(const T* b, KOff ko, ColOff co)
-      : base(b), k_off(ko), col_off(co) {}
-
-  __device__ __forceinline__ void fetch(int s) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int u = threadIdx.x + i * Cfg::kThreads;
-      const int kg = u % KG, cg = u / KG;
-      const int co = (u < N_UNITS) ? col_off(cg) : 0;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int ro = (u < N_UNITS) ? k_off(s, kg * 8 + m) : -1;
-        if (ro >= 0) oct_load(reg[i][m], base + ro + co);
-        else oct_zero(reg[i][m]);
-      }
-    }
-  }
-  __device__ __forceinline__ void put(T* stage) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int u = threadIdx.x + i * Cfg::kThreads;
-      if (u >= N_UNITS) continue;
-      const int kg = u % KG, cg = u / KG;
-      Oct<T> out[8];
-      oct_transpose(out, reg[i]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) oct_store(stage + (cg * 8 + c) * Cfg::LD + kg * 8, out[c]);
-    }
-  }
-};
-
-template <class Cfg, int COLS, class KOff, class ColOff>
-__device__ __forceinline__ TransLoader<Cfg, COLS, KOff, ColOff> make_trans(
-    const typename Cfg::T* base, KOff ko, ColOff co) {
-  return TransLoader<Cfg, COLS, KOff, ColOff>(base, ko, co);
+// ---------------------------------------------------------------------------
+// Low-level helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dma16(const void* g, char* lds_wave) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave, 16, 0, 0);
 }
 
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that also stops the compiler from moving memory
+// operations across it.  Waits for outstanding memory operations are
+// explicit (wait_vm / wait_lgkm0) at the call sites.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+}
+
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int mswz(int k) { return (k & 3) << 1; }
+
+// ---------------------------------------------------------------------------
+// Loaders (one DMA instruction fills 1 KB of a tile; wave w issues
+// instructions i = 0..NI-1 into tile bytes [(4 i + w) KB, (4 i + w + 1) KB)).
+// ---------------------------------------------------------------------------
+
+// K-major operand whose ROWS source rows are fixed over the k loop: row r's
+// k-values for slab s start at rowptr(r) + 128 s bytes.
+template <class Cfg, int ROWS>
+struct KLoad {
+  static_assert(ROWS % 32 == 0, "rows");
+  static constexpr int NI = ROWS / 32;
+  const char* p[NI];
+  int w;
+
+  template <class RowPtr>
+  __device__ __forceinline__ void init(RowPtr rowptr) {
+    w = wave_id();
+    const int L = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = (i * 4 + w) * 64 + L;
+      const int r = idx >> 3, pos = idx & 7;
+      p[i] = reinterpret_cast<const char*>(rowptr(r)) + ((pos ^ kswz(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(int s, char* tile) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(p[i] + s * 128, tile + (i * 4 + w) * 1024);
+  }
+};
+
+// MN-major operand with a fixed row stride (weights): row k of slab s is at
+// base + (s*BK + k) * ld_bytes; col_bytes(c) is the byte offset of logical
+// 16-byte chunk c of the tile row inside a source row.
+template <class Cfg, int COLS>
+struct MNLoad {
+  using T = typename Cfg::T;
+  static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
+  static constexpr int NI = Cfg::BK * RB / 4096;
+  static_assert(NI >= 1 && (Cfg::BK * RB) % 4096 == 0, "tile size");
+  const char* p[NI];
+  int64_t step;
+  int w;
+
+  template <class ColBytes>
+  __device__ __forceinline__ void init(const void* base, int64_t ld_bytes, ColBytes col_bytes) {
+    w = wave_id();
+    const int L = threadIdx.x & 63;
+    step = int64_t(Cfg::BK) * ld_bytes;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = (i * 4 + w) * 64 + L;
+      const int k = idx / CH, pos = idx % CH;
+      p[i] = reinterpret_cast<const char*>(base) + k * ld_bytes + col_bytes(pos ^ mswz(k));
+    }
+  }
+  __device__ __forceinline__ void issue(int s, char* tile) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(p[i] + s * step, tile + (i * 4 + w) * 1024);
+  }
+};
+
+// MN-major operand whose rows are an expert's slots (varlen-K): row k of
+// slab s is slot kb + s*BK + k, read from source row idx[slot] (GATHER) or
+// row slot; slots past the expert's end read its last slot and are zeroed in
+// LDS afterwards.  The gather indices are wave-uniform per row and are read
+// with scalar loads, so they do not count against the DMA wait counter.
+template <class Cfg, int COLS, bool GATHER>
+struct SlotLoad {
+  using T = typename Cfg::T;
+  static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
+  static constexpr int NI = Cfg::BK * RB / 4096;
+  static constexpr int RPI = 64 / CH;  // tile rows per DMA instruction
+  static_assert(NI >= 1 && RPI >= 1 && (!GATHER || RPI <= 4), "tile size");
+  const char* base;
+  const int32_t* idx;
+  int64_t ld_bytes;
+  int colb[NI];
+  int kb, klast, w, sub;
+
+  template <class ColBytes>
+  __device__ __forceinline__ void init(const void* b, int64_t ldb, ColBytes col_bytes,
+                                       const int32_t* index, int kbeg, int kend) {
+    base = reinterpret_cast<const char*>(b);
+    idx = index;
+    ld_bytes = ldb;
+    kb = kbeg;
+    klast = kend - 1;
+    w = wave_id();
+    const int L = threadIdx.x & 63;
+    sub = L / CH;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = (i * 4 + w) * 64 + L;
+      const int k = q / CH, pos = q % CH;
+      colb[i] = col_bytes(pos ^ mswz(k));
+    }
+  }
+  __device__ __forceinline__ void issue(int s, char* tile) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k0 = kb + s * Cfg::BK + (i * 4 + w) * RPI;  // wave-uniform
+      int row;
+      if constexpr (GATHER) {
+        int r[RPI];
+#pragma unroll
+        for (int q = 0; q < RPI; ++q) r[q] = idx[min(k0 + q, klast)];
+        row = r[0];
+#pragma unroll
+        for (int q = 1; q < RPI; ++q) row = (sub == q) ? r[q] : row;
+      } else {
+        row = min(k0 + sub, klast);
+      }
+      dma16(base + row * ld_bytes + colb[i], tile + (i * 4 + w) * 1024);
+    }
+  }
+};
+
+// Zero rows [valid, BK) of an MN-major tile of COLS elements (tail slab of a
+// varlen-K contraction).
+template <class Cfg, int COLS>
+__device__ __forceinline__ void zero_rows(char* tile, int valid) {
+  constexpr int RB = COLS * int(sizeof(typename Cfg::T));
+  const int start = valid * RB, end = Cfg::BK * RB;
+  for (int o = start + int(threadIdx.x) * 16; o < end; o += Cfg::kThreads * 16)
+    *reinterpret_cast<uint4*>(tile + o) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Fragment reads
+// ---------------------------------------------------------------------------
+// K-major: 8 k-values (k = 16 kc + 8 h ..) of tile row r.
+template <class T>
+__device__ __forceinline__ void frag_k(Oct<T>& f, const char* tile, int r, int kc, int h) {
+  constexpr int CPO = int(sizeof(T)) / 2;  // 16-byte chunks per octet
+  const int c0 = (kc * 2 + h) * CPO;
+#pragma unroll
+  for (int j = 0; j < CPO; ++j) {
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + r * 128 + (((c0 + j) ^ kswz(r)) << 4));
+    f.w[4 * j + 0] = v.x; f.w[4 * j + 1] = v.y; f.w[4 * j + 2] = v.z; f.w[4 * j + 3] = v.w;
+  }
+}
+
+// MN-major: 8 k-values of column cb + (lane % 32) for the 32-column block at
+// cb (bf16: two transposing reads; fp32: eight scalar reads).
+template <class T, int COLS>
+__device__ __forceinline__ void frag_mn(Oct<T>& f, const char* tile, int cb, int kc, int lane);
+
+template <class T, int COLS>
+__device__ __forceinline__ void frag_mn(Oct<T>& f, const char* tile, int cb, int kc, int lane) {
+  constexpr int RB = COLS * int(sizeof(T));
+  if constexpr (sizeof(T) == 2) {
+    const int g = lane >> 4, s = lane & 15, h = g >> 1;
+    const int c = cb + 16 * (g & 1) + 4 * (s & 3);  // column this lane points at
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = kc * 16 + h * 8 + half * 4 + (s >> 2);
+      const char* a = tile + k * RB + ((((c >> 3) ^ mswz(k))) << 4) + (c & 7) * 2;
+      const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a);
+      f.w[half * 2 + 0] = uint32_t(uint16_t(v[0])) | (uint32_t(uint16_t(v[1])) << 16);
+      f.w[half * 2 + 1] = uint32_t(uint16_t(v[2])) | (uint32_t(uint16_t(v[3])) << 16);
+    }
+  } else {
+    const int col = cb + (lane & 31), h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = kc * 16 + h * 8 + j;
+      const int byte = col * 4;
+      f.w[j] = *reinterpret_cast<const uint32_t*>(tile + k * RB +
+                                                  ((((byte >> 4) ^ mswz(k))) << 4) + (byte & 15));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Accumulators and the slab computation
+// ---------------------------------------------------------------------------
 template <class Cfg>
 struct Accum {
   using T = typename Cfg::T;
@@ -161,7 +291,7 @@ struct Accum {
   int wm, wn, lane;
 
   __device__ __forceinline__ void init() {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     lane = threadIdx.x & 63;
     wm = wave / Cfg::WGN;
     wn = wave % Cfg::WGN;
@@ -173,19 +303,26 @@ struct Accum {
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
   }
 
-  // One BK slab from LDS.
-  __device__ __forceinline__ void slab(const T* As, const T* Bs) {
+  // One BK slab: A tile (K-major if AK, else MN-major of BM columns) and B
+  // tile (K-major if BKM, else MN-major of BN columns).
+  template <bool AK, bool BKM>
+  __device__ __forceinline__ void slab(const char* As, const char* Bs) {
     const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int kc = 0; kc < Cfg::KCH; ++kc) {
       Oct<T> fa[Cfg::MB], fb[Cfg::NB];
-      const int ko = kc * 16 + h * 8;
 #pragma unroll
-      for (int a = 0; a < Cfg::MB; ++a)
-        oct_load(fa[a], As + (wm * Cfg::WTM + a * 32 + r32) * Cfg::LD + ko);
+      for (int a = 0; a < Cfg::MB; ++a) {
+        const int rb = wm * Cfg::WTM + a * 32;
+        if constexpr (AK) frag_k<T>(fa[a], As, rb + r32, kc, h);
+        else frag_mn<T, Cfg::BM>(fa[a], As, rb, kc, lane);
+      }
 #pragma unroll
-      for (int b = 0; b < Cfg::NB; ++b)
-        oct_load(fb[b], Bs + (Cfg::colblock(wn, b) + r32) * Cfg::LD + ko);
+      for (int b = 0; b < Cfg::NB; ++b) {
+        const int cb = Cfg::colblock(wn, b);
+        if constexpr (BKM) frag_k<T>(fb[b], Bs, cb + r32, kc, h);
+        else frag_mn<T, Cfg::BN>(fb[b], Bs, cb, kc, lane);
+      }
 #pragma unroll
       for (int a = 0; a < Cfg::MB; ++a)
 #pragma unroll
@@ -193,45 +330,72 @@ struct Accum {
     }
   }
 
-  // Tile-local row of block a for this lane, and tile-local first column of
-  // the 4-column group q (0..3) of block b.
+  // Tile row of block a for this lane; tile column of the 4-column group q.
   __device__ __forceinline__ int row(int a) const { return wm * Cfg::WTM + a * 32 + (lane & 31); }
   __device__ __forceinline__ int col(int b, int q) const {
     return Cfg::colblock(wn, b) + q * 8 + (lane >> 5) * 4;
   }
 };
 
-// Double-buffered main loop over `nslabs` BK-slabs: global loads of slab s+1
-// are in flight while slab s is multiplied from LDS.  One barrier per slab.
-template <class Cfg, class LA, class LB>
-__device__ __forceinline__ void mainloop(Accum<Cfg>& acc, typename Cfg::T* lds, int nslabs,
-                                         LA&& load_a, LB&& load_b) {
-  using T = typename Cfg::T;
-  T* As0 = lds;
-  T* As1 = lds + Cfg::A_ELEMS;
-  T* Bs0 = lds + 2 * Cfg::A_ELEMS;
-  T* Bs1 = Bs0 + Cfg::B_ELEMS;
-  if (nslabs <= 0) return;
-  load_a.fetch(0);
-  load_b.fetch(0);
-  load_a.put(As0);
-  load_b.put(Bs0);
-  __syncthreads();
-  for (int s = 0; s < nslabs; ++s) {
-    const bool more = s + 1 < nslabs;
-    if (more) {
-      load_a.fetch(s + 1);
-      load_b.fetch(s + 1);
-    }
-    if (s & 1) acc.slab(As1, Bs1);
-    else acc.slab(As0, Bs0);
-    if (more) {
-      load_a.put((s & 1) ? As0 : As1);
-      load_b.put((s & 1) ? Bs0 : Bs1);
-    }
-    __syncthreads();
+// One pipeline step: DMA for a later slab into `nxt` while slab s is
+// multiplied out of `cur`.  The two stages are distinct restrict pointers so
+// that the compiler can tell the DMA writes from the fragment reads (alias
+// scopes); otherwise it would wait for every outstanding DMA before the first
+// LDS read and the prefetch would be lost.
+template <class Cfg, bool AK, bool BKM, class LA, class LB, class Tail>
+__device__ __forceinline__ void pipeline_step(Accum<Cfg>& acc, const char* __restrict__ cur,
+                                              char* __restrict__ nxt, bool issue, int s_next,
+                                              int s, const LA& la, const LB& lb, Tail& tail) {
+  if (issue) {
+    la.issue(s_next, nxt);
+    lb.issue(s_next, nxt + Cfg::A_BYTES);
   }
+  tail(s, const_cast<char*>(cur));
+  acc.template slab<AK, BKM>(cur, cur + Cfg::A_BYTES);
 }
+
+// Multi-stage DMA pipeline over `nslabs` slabs.  Slab s lives in stage s % S;
+// at the top of iteration s the wave waits until its own DMA for slab s has
+// landed (later slabs may stay in flight), the barrier makes every wave's
+// part visible, and the DMA for slab s + S - 1 is issued into the stage that
+// was consumed in iteration s - 1.  `tail(s, stage)` may patch the stage
+// (it must end with its own wait + barrier if it writes LDS).
+template <class Cfg, bool AK, bool BKM, class LA, class LB, class Tail>
+__device__ __forceinline__ void pipeline(Accum<Cfg>& acc, char* lds, int nslabs, const LA& la,
+                                         const LB& lb, Tail&& tail) {
+  constexpr int S = Cfg::STAGES, NI = LA::NI + LB::NI;
+  static_assert(S >= 2 && S <= 4 && NI * (S - 2) < 64, "pipeline depth");
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) {
+    if (st < nslabs) {
+      char* sp = lds + st * Cfg::STAGE_BYTES;
+      la.issue(st, sp);
+      lb.issue(st, sp + Cfg::A_BYTES);
+    }
+  }
+  for (int s = 0; s < nslabs; ++s) {
+    const int ahead = min(S - 2, nslabs - 1 - s);  // slabs issued after slab s
+    if constexpr (S >= 4) {
+      if (ahead >= 2) wait_vm<2 * NI>();
+      else if (ahead == 1) wait_vm<NI>();
+      else wait_vm<0>();
+    } else if constexpr (S == 3) {
+      if (ahead >= 1) wait_vm<NI>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    barrier();
+    pipeline_step<Cfg, AK, BKM>(acc, lds + (s % S) * Cfg::STAGE_BYTES,
+                                lds + ((s + S - 1) % S) * Cfg::STAGE_BYTES, s + S - 1 < nslabs,
+                                s + S - 1, s, la, lb, tail);
+  }
+  barrier();
+}
+
+struct NoTail {
+  __device__ __forceinline__ void operator()(int, char*) const {}
+};
 
 // Spreads `work` logical tiles over the 8 XCDs in contiguous chunks:
 // workgroups are dispatched round-robin over XCDs, so block b runs on XCD

@@ -19,8 +19,11 @@ namespace {
 
 inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
 
+constexpr int kStages = 3;
+
 // BN == n: one workgroup owns whole rows of dA', so the dS row sums stay
 // inside the workgroup and are written once, in a fixed order.
+// A = gathered dO rows (K-major), B = W2_e rows (K-major, contraction over d).
 template <class T, int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(256) void k_dh(
     const T* __restrict__ dO, const T* __restrict__ W2, const T* __restrict__ H,
@@ -28,8 +31,8 @@ __global__ __launch_bounds__(256) void k_dh(
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
     const float* __restrict__ slot_weight, const int32_t* __restrict__ totals, int d) {
-  using Cfg = TileCfg<T, BM, BN, WGM, WGN>;
-  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  using Cfg = TileCfg<T, BM, BN, WGM, WGN, kStages>;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int n = BN, n2 = 2 * BN, SUB = kTileM / BM;
   const int lin = xcd_tile(blockIdx.x, totals[1] * SUB);
   if (lin < 0) return;
@@ -37,18 +40,20 @@ __global__ __launch_bounds__(256) void k_dh(
   const int e = tile_expert[mt], row0 = tile_row[mt] + (lin % SUB) * BM;
   const int rend = expert_offsets[e + 1];
   if (row0 >= rend) return;
+  const int tok0 = slot_token[row0];
 
-  DirectLoader<Cfg, BM> la;
-  la.init(dO, [&](int r) {
+  KLoad<Cfg, BM> la;
+  la.init([&](int r) {
     const int slot = row0 + r;
-    return slot < rend ? slot_token[slot] * d : -1;
+    return dO + int64_t(slot < rend ? slot_token[slot] : tok0) * d;
   });
-  DirectLoader<Cfg, BN> lb;
-  lb.init(W2 + int64_t(e) * n * d, [&](int j) { return j * d; });
+  const T* w2 = W2 + int64_t(e) * n * d;
+  KLoad<Cfg, BN> lb;
+  lb.init([&](int j) { return w2 + int64_t(j) * d; });
 
   Accum<Cfg> acc;
   acc.init();
-  mainloop(acc, lds, d / Cfg::BK, la, lb);
+  pipeline<Cfg, true, true>(acc, lds, d / Cfg::BK, la, lb, NoTail{});
 
   float* red = reinterpret_cast<float*>(lds);  // [WGN][BM] partial row sums
 #pragma unroll
@@ -101,14 +106,15 @@ __global__ __launch_bounds__(256) void k_dh(
   }
 }
 
+// A = dH rows (K-major), B = W1_e rows (K-major, contraction over 2n).
 template <class T, int BN>
 __global__ __launch_bounds__(256) void k_dxt(
     const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
     int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2>;
-  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages>;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   const int NT = d / BN, n2 = 2 * n;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
@@ -116,17 +122,18 @@ __global__ __launch_bounds__(256) void k_dxt(
   const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
   const int j0 = nt * BN;
 
-  DirectLoader<Cfg, kTileM> la;
-  la.init(dH, [&](int r) {
+  KLoad<Cfg, kTileM> la;
+  la.init([&](int r) {
     const int slot = row0 + r;
-    return slot < rend ? slot * n2 : -1;
+    return dH + int64_t(slot < rend ? slot : row0) * n2;
   });
-  DirectLoader<Cfg, BN> lb;
-  lb.init(W1 + int64_t(e) * d * n2, [&](int c) { return (j0 + c) * n2; });
+  const T* w1 = W1 + int64_t(e) * d * n2;
+  KLoad<Cfg, BN> lb;
+  lb.init([&](int c) { return w1 + int64_t(j0 + c) * n2; });
 
   Accum<Cfg> acc;
   acc.init();
-  mainloop(acc, lds, n2 / Cfg::BK, la, lb);
+  pipeline<Cfg, true, true>(acc, lds, n2 / Cfg::BK, la, lb, NoTail{});
 
 #pragma unroll
   for (int a = 0; a < Cfg::MB; ++a) {
@@ -177,71 +184,78 @@ __device__ __forceinline__ void store_tile(const Accum<Cfg>& acc, typename Cfg::
   }
 }
 
+// Zeroes the rows past the expert's last slot in the final, partial slab of
+// a varlen-K contraction (those rows were read from the last valid slot).
+template <class Cfg, int ACOLS, int BCOLS>
+struct VarlenTail {
+  int nslabs, valid;
+  __device__ __forceinline__ void operator()(int s, char* stage) const {
+    if (s != nslabs - 1 || valid == Cfg::BK) return;
+    zero_rows<Cfg, ACOLS>(stage, valid);
+    zero_rows<Cfg, BCOLS>(stage + Cfg::A_BYTES, valid);
+    wait_lgkm0();
+    barrier();
+  }
+};
+
+// dW1_e[i][j] = sum over the expert's slots k of X[tok_k][i] * dH[k][j]:
+// both operands MN-major, rows = slots (X rows gathered through slot_token).
 template <class T, int BN>
 __global__ __launch_bounds__(256) void k_dw1(
     const T* __restrict__ X, const T* __restrict__ dH, T* __restrict__ dW1,
     const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
     const int32_t* __restrict__ slot_token, int E, int d, int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2>;
-  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages>;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr int EPC = 16 / int(sizeof(T));
   const int n2 = 2 * n, TN = n2 / BN, PT = (d / kTileM) * TN;
   int e, tile;
   if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
   const int i0 = (tile / TN) * kTileM, j0 = (tile % TN) * BN;
   const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
+  const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
-  auto la = make_trans<Cfg, kTileM>(
-      X,
-      [=](int s, int k) {
-        const int slot = kb + s * Cfg::BK + k;
-        return slot < ke ? slot_token[slot] * d : -1;
-      },
-      [=](int cg) { return i0 + cg * 8; });
-  auto lb = make_trans<Cfg, BN>(
-      dH,
-      [=](int s, int k) {
-        const int slot = kb + s * Cfg::BK + k;
-        return slot < ke ? slot * n2 : -1;
-      },
-      [=](int cg) { return j0 + cg * 8; });
+  SlotLoad<Cfg, kTileM, true> la;
+  la.init(X, int64_t(d) * sizeof(T), [=](int c) { return int((i0 + c * EPC) * sizeof(T)); },
+          slot_token, kb, ke);
+  SlotLoad<Cfg, BN, false> lb;
+  lb.init(dH, int64_t(n2) * sizeof(T), [=](int c) { return int((j0 + c * EPC) * sizeof(T)); },
+          nullptr, kb, ke);
 
   Accum<Cfg> acc;
   acc.init();
-  mainloop(acc, lds, (ke - kb + Cfg::BK - 1) / Cfg::BK, la, lb);
+  VarlenTail<Cfg, kTileM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
+  pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
   store_tile(acc, dW1 + (int64_t(e) * d + i0) * n2 + j0, n2);
 }
 
+// dW2_e[i][j] = sum over the expert's slots k of As[k][i] * dO[tok_k][j].
 template <class T, int BM, int BN>
 __global__ __launch_bounds__(256) void k_dw2(
     const T* __restrict__ As, const T* __restrict__ dO, T* __restrict__ dW2,
     const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
     const int32_t* __restrict__ slot_token, int E, int d, int n) {
-  using Cfg = TileCfg<T, BM, BN, 2, 2>;
-  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  using Cfg = TileCfg<T, BM, BN, 2, 2, kStages>;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr int EPC = 16 / int(sizeof(T));
   const int TN = d / BN, PT = (n / BM) * TN;
   int e, tile;
   if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
   const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
   const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
+  const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
-  auto la = make_trans<Cfg, BM>(
-      As,
-      [=](int s, int k) {
-        const int slot = kb + s * Cfg::BK + k;
-        return slot < ke ? slot * n : -1;
-      },
-      [=](int cg) { return i0 + cg * 8; });
-  auto lb = make_trans<Cfg, BN>(
-      dO,
-      [=](int s, int k) {
-        const int slot = kb + s * Cfg::BK + k;
-        return slot < ke ? slot_token[slot] * d : -1;
-      },
-      [=](int cg) { return j0 + cg * 8; });
+  SlotLoad<Cfg, BM, false> la;
+  la.init(As, int64_t(n) * sizeof(T), [=](int c) { return int((i0 + c * EPC) * sizeof(T)); },
+          nullptr, kb, ke);
+  SlotLoad<Cfg, BN, true> lb;
+  lb.init(dO, int64_t(d) * sizeof(T), [=](int c) { return int((j0 + c * EPC) * sizeof(T)); },
+          slot_token, kb, ke);
 
   Accum<Cfg> acc;
   acc.init();
-  mainloop(acc, lds, (ke - kb + Cfg::BK - 1) / Cfg::BK, la, lb);
+  VarlenTail<Cfg, BM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
+  pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
   store_tile(acc, dW2 + (int64_t(e) * n + i0) * d + j0, d);
 }
 

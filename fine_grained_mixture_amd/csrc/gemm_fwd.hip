@@ -17,37 +17,42 @@
 namespace moe {
 namespace {
 
+constexpr int kStages = 3;
+
 // One workgroup computes a 128-row M tile against BN/2 gate columns and the
 // matching BN/2 up columns, so SiLU(gate) * up is formed in registers.
+// A = gathered X rows (K-major), B = W1_e columns (MN-major).
 template <class T, int BN>
 __global__ __launch_bounds__(256) void k_up_swiglu(
     const T* __restrict__ X, const T* __restrict__ W1, T* __restrict__ H, T* __restrict__ Aact,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
     const int32_t* __restrict__ totals, int d, int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2, true>;
-  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
-  constexpr int HALF = BN / 2;
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages, true>;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr int HALF = BN / 2, EPC = 16 / int(sizeof(T));
   const int NT = n / HALF;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
   const int mt = lin / NT, nt = lin % NT;
   const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
   const int j0 = nt * HALF, n2 = 2 * n;
+  const int tok0 = slot_token[row0];
 
-  DirectLoader<Cfg, kTileM> la;
-  la.init(X, [&](int r) {
+  KLoad<Cfg, kTileM> la;
+  la.init([&](int r) {
     const int slot = row0 + r;
-    return slot < rend ? slot_token[slot] * d : -1;
+    return X + int64_t(slot < rend ? slot_token[slot] : tok0) * d;
   });
-  const T* w1 = W1 + int64_t(e) * d * n2;
-  auto lb = make_trans<Cfg, BN>(
-      w1, [=](int s, int k) { return (s * Cfg::BK + k) * n2; },
-      [=](int cg) { return cg * 8 < HALF ? j0 + cg * 8 : n + j0 + cg * 8 - HALF; });
+  MNLoad<Cfg, BN> lb;
+  lb.init(W1 + int64_t(e) * d * n2, int64_t(n2) * sizeof(T), [=](int c) {
+    const int ce = c * EPC;
+    return int((ce < HALF ? j0 + ce : n + j0 + ce - HALF) * sizeof(T));
+  });
 
   Accum<Cfg> acc;
   acc.init();
-  mainloop(acc, lds, d / Cfg::BK, la, lb);
+  pipeline<Cfg, true, false>(acc, lds, d / Cfg::BK, la, lb, NoTail{});
 
 #pragma unroll
   for (int a = 0; a < Cfg::MB; ++a) {
@@ -77,14 +82,16 @@ __global__ __launch_bounds__(256) void k_up_swiglu(
   }
 }
 
+// A = activation rows (K-major), B = W2_e columns (MN-major).
 template <class T, int BN>
 __global__ __launch_bounds__(256) void k_down(
     const T* __restrict__ Aact, const T* __restrict__ W2, T* __restrict__ Y,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
     int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2>;
-  __shared__ __attribute__((aligned(16))) T lds[Cfg::LDS_ELEMS];
+  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages>;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr int EPC = 16 / int(sizeof(T));
   const int NT = d / BN;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
@@ -92,18 +99,18 @@ __global__ __launch_bounds__(256) void k_down(
   const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
   const int j0 = nt * BN;
 
-  DirectLoader<Cfg, kTileM> la;
-  la.init(Aact, [&](int r) {
+  KLoad<Cfg, kTileM> la;
+  la.init([&](int r) {
     const int slot = row0 + r;
-    return slot < rend ? slot * n : -1;
+    return Aact + int64_t(slot < rend ? slot : row0) * n;
   });
-  const T* w2 = W2 + int64_t(e) * n * d;
-  auto lb = make_trans<Cfg, BN>(
-      w2, [=](int s, int k) { return (s * Cfg::BK + k) * d; }, [=](int cg) { return j0 + cg * 8; });
+  MNLoad<Cfg, BN> lb;
+  lb.init(W2 + int64_t(e) * n * d, int64_t(d) * sizeof(T),
+          [=](int c) { return int((j0 + c * EPC) * sizeof(T)); });
 
   Accum<Cfg> acc;
   acc.init();
-  mainloop(acc, lds, n / Cfg::BK, la, lb);
+  pipeline<Cfg, true, false>(acc, lds, n / Cfg::BK, la, lb, NoTail{});
 
 #pragma unroll
   for (int a = 0; a < Cfg::MB; ++a) {
