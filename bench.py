@@ -125,6 +125,10 @@ def main():
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
     ap.add_argument("--mode", default="tr", choices=["tr", "tc"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (known HBM "
+                         "traffic: 1 GiB read + 1 GiB written per launch), to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -132,9 +136,18 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    sh = SHAPES[args.config]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
+                          "launches": 5}))
+        return
+    sh = SHAPES[args.config]
     inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)
     X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
     p = moe.problem(sh.T, sh.d, sh.n, sh.E, sh.K, sh.M, torch.bfloat16, args.mode)

@@ -42,10 +42,15 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    objs = [os.path.join(OBJDIR, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+def build(verbose: bool = False, jobs: int | None = None, defines=(), lib: str = LIB,
+          objdir: str = OBJDIR) -> str:
+    """Compiles every source and links `lib`.  `defines` are extra -D
+    options (e.g. MOE_TILE_VARIANT=n to pick another GEMM tile shape)."""
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
+    dflags = [f"-D{d}" for d in defines]
+    cmds = [[HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for cmd, msg in zip(cmds, ex.map(_run, cmds)):
@@ -53,10 +58,10 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
                 print(" ".join(cmd[-3:]), file=sys.stderr)
             if msg.strip() and verbose:
                 print(msg, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

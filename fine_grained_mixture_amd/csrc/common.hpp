@@ -22,12 +22,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even; NaN stays NaN (quiet bit set).
+// Round-to-nearest-even (the hardware v_cvt_pk_bf16_f32 conversion).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <class T> struct Elem;
@@ -129,7 +126,11 @@ __device__ __forceinline__ void mma16(f32x16_t& acc, const Oct<float>& a, const 
 // ---------------------------------------------------------------------------
 // Small helpers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Logistic function with the hardware exp and reciprocal (about 1 ulp each,
+// far below the bf16 rounding of every value it feeds).
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 template <class T>
 __host__ __device__ constexpr T cdiv(T a, T b) { return (a + b - 1) / b; }
@@ -141,6 +142,7 @@ struct RouteWs {
   size_t bits_e;   // uint32 [E][nw] selection bitmap, expert-major (nw = ceil(T/32))
   size_t bits_t;   // uint32 [T][W]  selection bitmap, token-major (W = ceil(E/32))
   size_t wbase;    // int32  [E][nw] slots of expert e in words before w
+  size_t block_sum;  // int32 [ceil(T/256)] slots per block of 256 tokens
   size_t total;
   __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
   __host__ __device__ static RouteWs make(int64_t T, int64_t E) {
@@ -151,6 +153,7 @@ struct RouteWs {
     w.bits_e = o; o = align(o + size_t(E) * nw * 4);
     w.bits_t = o; o = align(o + size_t(T) * W * 4);
     w.wbase = o;  o = align(o + size_t(E) * nw * 4);
+    w.block_sum = o; o = align(o + size_t((T + 255) / 256) * 4);
     w.total = o;
     return w;
   }

@@ -3,8 +3,9 @@
 // DMA pipeline, and bf16/fp32 MFMA fragment reads for both operand layouts.
 //
 // Operand layouts.  Every GEMM computes C[i][j] = sum_k A[i][k] B[k][j] for
-// one BM x BN output tile, BK = 128 bytes of k per slab (64 bf16 / 32 fp32).
-//   K-major tile   one LDS row of 128 B per output row (i of A, j of B),
+// one BM x BN output tile, KB bytes of k per slab (KB = 64 or 128; BK = KB /
+// sizeof(T) k-values).
+//   K-major tile   one LDS row of KB bytes per output row (i of A, j of B),
 //                  holding that row's BK k-values.  Used where the source
 //                  rows hold k contiguously (X, dO, A, dH, and the weights
 //                  when the contraction runs along their rows).
@@ -19,10 +20,15 @@
 // Tiles are unpadded; bank conflicts are avoided by XOR-swizzling the 16-byte
 // chunks of each row (the lane that fills a physical chunk fetches the
 // logical chunk that belongs there):
-//   K-major:   physical chunk = logical chunk ^ ((row >> 1) & 7)
-//   MN-major:  physical chunk = logical chunk ^ ((k & 3) << 1)
-// so that the 16 rows read by 16 lanes (K-major), or the 4 rows x 32 bytes
-// read by one transposing LDS read (MN-major), fall on distinct banks.
+//   K-major:   physical chunk = logical chunk ^ ((row >> 1) & 7)   (KB = 128)
+//              physical chunk = logical chunk ^ ((row >> 2) & 3)   (KB = 64)
+//   MN-major:  physical chunk = logical chunk ^ ((k & 3) << 2)  (rows >= 256 B)
+//              physical chunk = logical chunk ^ (((k >> 1) & 1) << 2)  (128 B)
+// The LDS has 64 banks of 4 bytes.  A 16-byte read is serviced 16 lanes at
+// a time: the 16 consecutive rows of a K-major fragment land in distinct
+// banks.  A transposing 8-byte read is serviced 32 lanes at a time: 4 rows x
+// 64 contiguous bytes, and the MN-major swizzle moves whole 64-byte windows
+// so those 4 windows cover all 256 bytes of banks.
 //
 // Fragment reads.  A 32x32x16 bf16 MFMA takes, in lane l, 8 consecutive
 // k-values of row l % 32 (k half l / 32).  K-major tiles give them with one
@@ -44,20 +50,23 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-template <class T_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool PAIRED_ = false>
+template <class T_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_, int KB_ = 128,
+          bool PAIRED_ = false>
 struct TileCfg {
   using T = T_;
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, KB = KB_;
+  static_assert(KB == 64 || KB == 128, "slab bytes");
   static constexpr bool PAIRED = PAIRED_;  // B columns = [gate half | up half]
-  static constexpr int kThreads = 256;
-  static_assert(WGM * WGN == 4, "four waves per workgroup");
-  static constexpr int BK = 128 / int(sizeof(T));  // k-values per slab (128 B)
+  static constexpr int NW = WGM * WGN;  // waves per workgroup
+  static constexpr int kThreads = 64 * NW;
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  static constexpr int BK = KB / int(sizeof(T));  // k-values per slab
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int MB = WTM / 32, NB = WTN / 32;
   static_assert(MB >= 1 && NB >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(!PAIRED || NB % 2 == 0, "paired tiles split each wave's columns");
   static constexpr int KCH = BK / 16;  // 16-wide k chunks per slab
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   // the requested depth, or the deepest that fits in the 160 KB of LDS
   static constexpr int STAGES =
@@ -104,20 +113,30 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
 }
 
-__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int mswz(int k) { return (k & 3) << 1; }
+template <int KB>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (KB == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+template <int CH>  // 16-byte chunks per MN-major row
+__device__ __forceinline__ int mswz(int k) {
+  static_assert(CH >= 8, "MN-major rows of at least 128 bytes");
+  if constexpr (CH >= 16) return (k & 3) << 2;
+  else return ((k >> 1) & 1) << 2;
+}
 
 // ---------------------------------------------------------------------------
-// Loaders (one DMA instruction fills 1 KB of a tile; wave w issues
-// instructions i = 0..NI-1 into tile bytes [(4 i + w) KB, (4 i + w + 1) KB)).
+// Loaders (one DMA instruction fills 1 KB of a tile; wave w of NW issues
+// instructions i = 0..NI-1 into tile bytes [(NW i + w) KB, (NW i + w + 1) KB)).
 // ---------------------------------------------------------------------------
 
 // K-major operand whose ROWS source rows are fixed over the k loop: row r's
-// k-values for slab s start at rowptr(r) + 128 s bytes.
+// k-values for slab s start at rowptr(r) + KB s bytes.
 template <class Cfg, int ROWS>
 struct KLoad {
-  static_assert(ROWS % 32 == 0, "rows");
-  static constexpr int NI = ROWS / 32;
+  static constexpr int KB = Cfg::KB, CPR = KB / 16;  // 16-byte chunks per row
+  static_assert((ROWS * KB) % (Cfg::kThreads * 16) == 0, "rows");
+  static constexpr int NI = ROWS * KB / (Cfg::kThreads * 16);
   const char* p[NI];
   int w;
 
@@ -127,14 +146,14 @@ struct KLoad {
     const int L = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int idx = (i * 4 + w) * 64 + L;
-      const int r = idx >> 3, pos = idx & 7;
-      p[i] = reinterpret_cast<const char*>(rowptr(r)) + ((pos ^ kswz(r)) << 4);
+      const int idx = (i * Cfg::NW + w) * 64 + L;
+      const int r = idx / CPR, pos = idx % CPR;
+      p[i] = reinterpret_cast<const char*>(rowptr(r)) + ((pos ^ kswz<KB>(r)) << 4);
     }
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(p[i] + s * 128, tile + (i * 4 + w) * 1024);
+    for (int i = 0; i < NI; ++i) dma16(p[i] + s * KB, tile + (i * Cfg::NW + w) * 1024);
   }
 };
 
@@ -145,8 +164,8 @@ template <class Cfg, int COLS>
 struct MNLoad {
   using T = typename Cfg::T;
   static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
-  static constexpr int NI = Cfg::BK * RB / 4096;
-  static_assert(NI >= 1 && (Cfg::BK * RB) % 4096 == 0, "tile size");
+  static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
+  static_assert(NI >= 1 && (Cfg::BK * RB) % (Cfg::kThreads * 16) == 0, "tile size");
   const char* p[NI];
   int64_t step;
   int w;
@@ -158,14 +177,14 @@ struct MNLoad {
     step = int64_t(Cfg::BK) * ld_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int idx = (i * 4 + w) * 64 + L;
+      const int idx = (i * Cfg::NW + w) * 64 + L;
       const int k = idx / CH, pos = idx % CH;
-      p[i] = reinterpret_cast<const char*>(base) + k * ld_bytes + col_bytes(pos ^ mswz(k));
+      p[i] = reinterpret_cast<const char*>(base) + k * ld_bytes + col_bytes(pos ^ mswz<CH>(k));
     }
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(p[i] + s * step, tile + (i * 4 + w) * 1024);
+    for (int i = 0; i < NI; ++i) dma16(p[i] + s * step, tile + (i * Cfg::NW + w) * 1024);
   }
 };
 
@@ -178,7 +197,7 @@ template <class Cfg, int COLS, bool GATHER>
 struct SlotLoad {
   using T = typename Cfg::T;
   static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
-  static constexpr int NI = Cfg::BK * RB / 4096;
+  static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
   static constexpr int RPI = 64 / CH;  // tile rows per DMA instruction
   static_assert(NI >= 1 && RPI >= 1 && (!GATHER || RPI <= 4), "tile size");
   const char* base;
@@ -200,15 +219,15 @@ struct SlotLoad {
     sub = L / CH;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = (i * 4 + w) * 64 + L;
+      const int q = (i * Cfg::NW + w) * 64 + L;
       const int k = q / CH, pos = q % CH;
-      colb[i] = col_bytes(pos ^ mswz(k));
+      colb[i] = col_bytes(pos ^ mswz<CH>(k));
     }
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int k0 = kb + s * Cfg::BK + (i * 4 + w) * RPI;  // wave-uniform
+      const int k0 = kb + s * Cfg::BK + (i * Cfg::NW + w) * RPI;  // wave-uniform
       int row;
       if constexpr (GATHER) {
         int r[RPI];
@@ -220,7 +239,7 @@ struct SlotLoad {
       } else {
         row = min(k0 + sub, klast);
       }
-      dma16(base + row * ld_bytes + colb[i], tile + (i * 4 + w) * 1024);
+      dma16(base + row * ld_bytes + colb[i], tile + (i * Cfg::NW + w) * 1024);
     }
   }
 };
@@ -239,13 +258,14 @@ __device__ __forceinline__ void zero_rows(char* tile, int valid) {
 // Fragment reads
 // ---------------------------------------------------------------------------
 // K-major: 8 k-values (k = 16 kc + 8 h ..) of tile row r.
-template <class T>
+template <class T, int KB>
 __device__ __forceinline__ void frag_k(Oct<T>& f, const char* tile, int r, int kc, int h) {
   constexpr int CPO = int(sizeof(T)) / 2;  // 16-byte chunks per octet
   const int c0 = (kc * 2 + h) * CPO;
 #pragma unroll
   for (int j = 0; j < CPO; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(tile + r * 128 + (((c0 + j) ^ kswz(r)) << 4));
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(tile + r * KB + (((c0 + j) ^ kswz<KB>(r)) << 4));
     f.w[4 * j + 0] = v.x; f.w[4 * j + 1] = v.y; f.w[4 * j + 2] = v.z; f.w[4 * j + 3] = v.w;
   }
 }
@@ -257,14 +277,14 @@ __device__ __forceinline__ void frag_mn(Oct<T>& f, const char* tile, int cb, int
 
 template <class T, int COLS>
 __device__ __forceinline__ void frag_mn(Oct<T>& f, const char* tile, int cb, int kc, int lane) {
-  constexpr int RB = COLS * int(sizeof(T));
+  constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
   if constexpr (sizeof(T) == 2) {
     const int g = lane >> 4, s = lane & 15, h = g >> 1;
     const int c = cb + 16 * (g & 1) + 4 * (s & 3);  // column this lane points at
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int k = kc * 16 + h * 8 + half * 4 + (s >> 2);
-      const char* a = tile + k * RB + ((((c >> 3) ^ mswz(k))) << 4) + (c & 7) * 2;
+      const char* a = tile + k * RB + ((((c >> 3) ^ mswz<CH>(k))) << 4) + (c & 7) * 2;
       const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a);
       f.w[half * 2 + 0] = uint32_t(uint16_t(v[0])) | (uint32_t(uint16_t(v[1])) << 16);
       f.w[half * 2 + 1] = uint32_t(uint16_t(v[2])) | (uint32_t(uint16_t(v[3])) << 16);
@@ -276,7 +296,7 @@ __device__ __forceinline__ void frag_mn(Oct<T>& f, const char* tile, int cb, int
       const int k = kc * 16 + h * 8 + j;
       const int byte = col * 4;
       f.w[j] = *reinterpret_cast<const uint32_t*>(tile + k * RB +
-                                                  ((((byte >> 4) ^ mswz(k))) << 4) + (byte & 15));
+                                                  ((((byte >> 4) ^ mswz<CH>(k))) << 4) + (byte & 15));
     }
   }
 }
@@ -303,30 +323,41 @@ struct Accum {
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
   }
 
-  // One BK slab: A tile (K-major if AK, else MN-major of BM columns) and B
-  // tile (K-major if BKM, else MN-major of BN columns).
+  // Fragments of k chunk kc: A tile (K-major if AK, else MN-major of BM
+  // columns) and B tile (K-major if BKM, else MN-major of BN columns).
   template <bool AK, bool BKM>
-  __device__ __forceinline__ void slab(const char* As, const char* Bs) {
+  __device__ __forceinline__ void frags(Oct<T> (&fa)[Cfg::MB], Oct<T> (&fb)[Cfg::NB],
+                                        const char* As, const char* Bs, int kc) const {
     const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
+    for (int a = 0; a < Cfg::MB; ++a) {
+      const int rb = wm * Cfg::WTM + a * 32;
+      if constexpr (AK) frag_k<T, Cfg::KB>(fa[a], As, rb + r32, kc, h);
+      else frag_mn<T, Cfg::BM>(fa[a], As, rb, kc, lane);
+    }
+#pragma unroll
+    for (int b = 0; b < Cfg::NB; ++b) {
+      const int cb = Cfg::colblock(wn, b);
+      if constexpr (BKM) frag_k<T, Cfg::KB>(fb[b], Bs, cb + r32, kc, h);
+      else frag_mn<T, Cfg::BN>(fb[b], Bs, cb, kc, lane);
+    }
+  }
+
+  // One slab: the fragments of chunk kc + 1 are read while the MFMAs of
+  // chunk kc run.
+  template <bool AK, bool BKM>
+  __device__ __forceinline__ void slab(const char* As, const char* Bs) {
+    Oct<T> fa[2][Cfg::MB], fb[2][Cfg::NB];
+    frags<AK, BKM>(fa[0], fb[0], As, Bs, 0);
+#pragma unroll
     for (int kc = 0; kc < Cfg::KCH; ++kc) {
-      Oct<T> fa[Cfg::MB], fb[Cfg::NB];
-#pragma unroll
-      for (int a = 0; a < Cfg::MB; ++a) {
-        const int rb = wm * Cfg::WTM + a * 32;
-        if constexpr (AK) frag_k<T>(fa[a], As, rb + r32, kc, h);
-        else frag_mn<T, Cfg::BM>(fa[a], As, rb, kc, lane);
-      }
-#pragma unroll
-      for (int b = 0; b < Cfg::NB; ++b) {
-        const int cb = Cfg::colblock(wn, b);
-        if constexpr (BKM) frag_k<T>(fb[b], Bs, cb + r32, kc, h);
-        else frag_mn<T, Cfg::BN>(fb[b], Bs, cb, kc, lane);
-      }
+      if (kc + 1 < Cfg::KCH) frags<AK, BKM>(fa[(kc + 1) & 1], fb[(kc + 1) & 1], As, Bs, kc + 1);
+      // keep those reads ahead of this chunk's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < Cfg::MB; ++a)
 #pragma unroll
-        for (int b = 0; b < Cfg::NB; ++b) mma16(acc[a][b], fb[b], fa[a]);
+        for (int b = 0; b < Cfg::NB; ++b) mma16(acc[a][b], fb[kc & 1][b], fa[kc & 1][a]);
     }
   }
 

@@ -13,26 +13,25 @@
 //   k_dw2   dW2_e = (s*A)_e^T dO[I_e]    (varlen-K)
 #include "gemm.hpp"
 #include "internal.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 namespace {
 
 inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
 
-constexpr int kStages = 3;
-
 // BN == n: one workgroup owns whole rows of dA', so the dS row sums stay
 // inside the workgroup and are written once, in a fixed order.
 // A = gathered dO rows (K-major), B = W2_e rows (K-major, contraction over d).
-template <class T, int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(256) void k_dh(
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dh(
     const T* __restrict__ dO, const T* __restrict__ W2, const T* __restrict__ H,
     T* __restrict__ dH, T* __restrict__ As, float* __restrict__ dS,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
     const float* __restrict__ slot_weight, const int32_t* __restrict__ totals, int d) {
-  using Cfg = TileCfg<T, BM, BN, WGM, WGN, kStages>;
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, WGN = Cfg::WGN;
   constexpr int n = BN, n2 = 2 * BN, SUB = kTileM / BM;
   const int lin = xcd_tile(blockIdx.x, totals[1] * SUB);
   if (lin < 0) return;
@@ -95,7 +94,7 @@ __global__ __launch_bounds__(256) void k_dh(
     if (acc.lane < 32) red[acc.wn * BM + i] = part;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < BM; i += 256) {
+  for (int i = threadIdx.x; i < BM; i += Cfg::kThreads) {
     const int slot = row0 + i;
     if (slot < rend) {
       float sum = 0.0f;
@@ -107,14 +106,15 @@ __global__ __launch_bounds__(256) void k_dh(
 }
 
 // A = dH rows (K-major), B = W1_e rows (K-major, contraction over 2n).
-template <class T, int BN>
-__global__ __launch_bounds__(256) void k_dxt(
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
     const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
     int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages>;
+  static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  constexpr int BN = Cfg::BN;
   const int NT = d / BN, n2 = 2 * n;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
@@ -200,22 +200,21 @@ struct VarlenTail {
 
 // dW1_e[i][j] = sum over the expert's slots k of X[tok_k][i] * dH[k][j]:
 // both operands MN-major, rows = slots (X rows gathered through slot_token).
-template <class T, int BN>
-__global__ __launch_bounds__(256) void k_dw1(
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
     const T* __restrict__ X, const T* __restrict__ dH, T* __restrict__ dW1,
     const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
     const int32_t* __restrict__ slot_token, int E, int d, int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages>;
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
-  constexpr int EPC = 16 / int(sizeof(T));
-  const int n2 = 2 * n, TN = n2 / BN, PT = (d / kTileM) * TN;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, EPC = 16 / int(sizeof(T));
+  const int n2 = 2 * n, TN = n2 / BN, PT = (d / BM) * TN;
   int e, tile;
   if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
-  const int i0 = (tile / TN) * kTileM, j0 = (tile % TN) * BN;
+  const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
   const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
-  SlotLoad<Cfg, kTileM, true> la;
+  SlotLoad<Cfg, BM, true> la;
   la.init(X, int64_t(d) * sizeof(T), [=](int c) { return int((i0 + c * EPC) * sizeof(T)); },
           slot_token, kb, ke);
   SlotLoad<Cfg, BN, false> lb;
@@ -224,20 +223,19 @@ __global__ __launch_bounds__(256) void k_dw1(
 
   Accum<Cfg> acc;
   acc.init();
-  VarlenTail<Cfg, kTileM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
+  VarlenTail<Cfg, BM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
   pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
   store_tile(acc, dW1 + (int64_t(e) * d + i0) * n2 + j0, n2);
 }
 
 // dW2_e[i][j] = sum over the expert's slots k of As[k][i] * dO[tok_k][j].
-template <class T, int BM, int BN>
-__global__ __launch_bounds__(256) void k_dw2(
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
     const T* __restrict__ As, const T* __restrict__ dO, T* __restrict__ dW2,
     const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
     const int32_t* __restrict__ slot_token, int E, int d, int n) {
-  using Cfg = TileCfg<T, BM, BN, 2, 2, kStages>;
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
-  constexpr int EPC = 16 / int(sizeof(T));
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, EPC = 16 / int(sizeof(T));
   const int TN = d / BN, PT = (n / BM) * TN;
   int e, tile;
   if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
@@ -259,83 +257,61 @@ __global__ __launch_bounds__(256) void k_dw2(
   store_tile(acc, dW2 + (int64_t(e) * n + i0) * d + j0, d);
 }
 
-template <class T>
-hipError_t dh_t(const LayerArgs& a, const void* dO, const void* W2, const void* H, void* dH,
-                void* As, float* dS, hipStream_t st) {
-  const T* o = static_cast<const T*>(dO);
-  const T* w = static_cast<const T*>(W2);
-  const T* h = static_cast<const T*>(H);
-  T* dh = static_cast<T*>(dH);
-  T* as = static_cast<T*>(As);
-#define MOE_DH(BM, BN, WGM, WGN)                                                              \
-  hipLaunchKernelGGL((k_dh<T, BM, BN, WGM, WGN>), dim3(grid_for(a.tile_cap * (kTileM / BM))), \
-                     dim3(256), 0, st, o, w, h, dh, as, dS, a.tile_expert, a.tile_row,        \
-                     a.expert_offsets, a.slot_token, a.slot_weight, a.totals, a.d)
-  switch (a.n) {
-    case 64: MOE_DH(128, 64, 4, 1); break;
-    case 128: MOE_DH(128, 128, 2, 2); break;
-    case 256: MOE_DH(128, 256, 2, 2); break;
-    case 384: MOE_DH(64, 384, 1, 4); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef MOE_DH
-  return hipGetLastError();
+template <class Cfg>
+void dh_launch(const LayerArgs& a, const void* dO, const void* W2, const void* H, void* dH,
+               void* As, float* dS, hipStream_t st) {
+  using T = typename Cfg::T;
+  hipLaunchKernelGGL((k_dh<Cfg>), dim3(grid_for(a.tile_cap * (kTileM / Cfg::BM))),
+                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dO),
+                     static_cast<const T*>(W2), static_cast<const T*>(H), static_cast<T*>(dH),
+                     static_cast<T*>(As), dS, a.tile_expert, a.tile_row, a.expert_offsets,
+                     a.slot_token, a.slot_weight, a.totals, a.d);
 }
 
 template <class T>
-hipError_t dxt_t(const LayerArgs& a, const void* dH, const void* W1, void* dXt, hipStream_t st) {
-  const T* dh = static_cast<const T*>(dH);
-  const T* w = static_cast<const T*>(W1);
-  T* o = static_cast<T*>(dXt);
-  if (sizeof(T) == 2 && a.d % 256 == 0)
-    hipLaunchKernelGGL((k_dxt<T, 256>), dim3(grid_for(a.tile_cap * (a.d / 256))), dim3(256), 0,
-                       st, dh, w, o, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
-                       a.n);
-  else
-    hipLaunchKernelGGL((k_dxt<T, 128>), dim3(grid_for(a.tile_cap * (a.d / 128))), dim3(256), 0,
-                       st, dh, w, o, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
-                       a.n);
+hipError_t dh_t(const LayerArgs& a, const void* dO, const void* W2, const void* H, void* dH,
+                void* As, float* dS, hipStream_t st) {
+  switch (a.n) {
+    case 64: dh_launch<TileCfg<T, 128, 64, 4, 1, 3>>(a, dO, W2, H, dH, As, dS, st); break;
+    case 128: dh_launch<TileCfg<T, 128, 128, 2, 2, 3>>(a, dO, W2, H, dH, As, dS, st); break;
+    case 256:
+      if constexpr (sizeof(T) == 2) dh_launch<DhWide>(a, dO, W2, H, dH, As, dS, st);
+      else dh_launch<TileCfg<T, 128, 256, 2, 2, 3>>(a, dO, W2, H, dH, As, dS, st);
+      break;
+    case 384: dh_launch<TileCfg<T, 64, 384, 1, 4, 3>>(a, dO, W2, H, dH, As, dS, st); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+template <class Cfg>
+void dxt_launch(const LayerArgs& a, const void* dH, const void* W1, void* dXt, hipStream_t st) {
+  using T = typename Cfg::T;
+  hipLaunchKernelGGL((k_dxt<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
+                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dH),
+                     static_cast<const T*>(W1), static_cast<T*>(dXt), a.tile_expert, a.tile_row,
+                     a.expert_offsets, a.totals, a.d, a.n);
 }
 
 inline unsigned varlen_k_grid(int E, int PT) { return unsigned(8 * ((E + 7) / 8) * PT); }
 
-template <class T>
-hipError_t dw1_t(const LayerArgs& a, const void* X, const void* dH, void* dW1, hipStream_t st) {
-  const T* x = static_cast<const T*>(X);
-  const T* dh = static_cast<const T*>(dH);
-  T* o = static_cast<T*>(dW1);
-  const int n2 = 2 * a.n;
-  if (sizeof(T) == 2 && n2 % 256 == 0)
-    hipLaunchKernelGGL((k_dw1<T, 256>), dim3(varlen_k_grid(a.E, (a.d / kTileM) * (n2 / 256))),
-                       dim3(256), 0, st, x, dh, o, a.expert_order, a.expert_offsets, a.slot_token,
-                       a.E, a.d, a.n);
-  else
-    hipLaunchKernelGGL((k_dw1<T, 128>), dim3(varlen_k_grid(a.E, (a.d / kTileM) * (n2 / 128))),
-                       dim3(256), 0, st, x, dh, o, a.expert_order, a.expert_offsets, a.slot_token,
-                       a.E, a.d, a.n);
-  return hipGetLastError();
+template <class Cfg>
+void dw1_launch(const LayerArgs& a, const void* X, const void* dH, void* dW1, hipStream_t st) {
+  using T = typename Cfg::T;
+  hipLaunchKernelGGL((k_dw1<Cfg>),
+                     dim3(varlen_k_grid(a.E, (a.d / Cfg::BM) * (2 * a.n / Cfg::BN))),
+                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
+                     static_cast<const T*>(dH), static_cast<T*>(dW1), a.expert_order,
+                     a.expert_offsets, a.slot_token, a.E, a.d, a.n);
 }
 
-template <class T>
-hipError_t dw2_t(const LayerArgs& a, const void* As, const void* dO, void* dW2, hipStream_t st) {
-  const T* as = static_cast<const T*>(As);
-  const T* o = static_cast<const T*>(dO);
-  T* w = static_cast<T*>(dW2);
-#define MOE_DW2(BM, BN)                                                                      \
-  hipLaunchKernelGGL((k_dw2<T, BM, BN>), dim3(varlen_k_grid(a.E, (a.n / BM) * (a.d / BN))), \
-                     dim3(256), 0, st, as, o, w, a.expert_order, a.expert_offsets,          \
-                     a.slot_token, a.E, a.d, a.n)
-  const bool wide = sizeof(T) == 2 && a.d % 256 == 0;
-  if (a.n % 128 == 0) {
-    if (wide) MOE_DW2(128, 256);
-    else MOE_DW2(128, 128);
-  } else {
-    if (wide) MOE_DW2(64, 256);
-    else MOE_DW2(64, 128);
-  }
-#undef MOE_DW2
-  return hipGetLastError();
+template <class Cfg>
+void dw2_launch(const LayerArgs& a, const void* As, const void* dO, void* dW2, hipStream_t st) {
+  using T = typename Cfg::T;
+  hipLaunchKernelGGL((k_dw2<Cfg>), dim3(varlen_k_grid(a.E, (a.n / Cfg::BM) * (a.d / Cfg::BN))),
+                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(As),
+                     static_cast<const T*>(dO), static_cast<T*>(dW2), a.expert_order,
+                     a.expert_offsets, a.slot_token, a.E, a.d, a.n);
 }
 
 }  // namespace
@@ -345,17 +321,41 @@ hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const v
   return a.f32 ? dh_t<float>(a, dO, W2, H, dH, As, dS, st)
                : dh_t<bf16_t>(a, dO, W2, H, dH, As, dS, st);
 }
+
 hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
                       hipStream_t st) {
-  return a.f32 ? dxt_t<float>(a, dH, W1, dXt, st) : dxt_t<bf16_t>(a, dH, W1, dXt, st);
+  if (a.f32) dxt_launch<TileCfg<float, kTileM, 128, 2, 2, 3>>(a, dH, W1, dXt, st);
+  else if (a.d % 512 == 0) dxt_launch<RowsWide>(a, dH, W1, dXt, st);
+  else if (a.d % 256 == 0) dxt_launch<RowsMid>(a, dH, W1, dXt, st);
+  else dxt_launch<RowsNarrow>(a, dH, W1, dXt, st);
+  return hipGetLastError();
 }
+
 hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1,
                       hipStream_t st) {
-  return a.f32 ? dw1_t<float>(a, X, dH, dW1, st) : dw1_t<bf16_t>(a, X, dH, dW1, st);
+  const int n2 = 2 * a.n;
+  if (a.f32) dw1_launch<TileCfg<float, 128, 128, 2, 2, 3>>(a, X, dH, dW1, st);
+  else if (a.d % 256 == 0 && n2 % 256 == 0) dw1_launch<GradSquare>(a, X, dH, dW1, st);
+  else if (n2 % 256 == 0) dw1_launch<GradTall>(a, X, dH, dW1, st);
+  else dw1_launch<GradSmall>(a, X, dH, dW1, st);
+  return hipGetLastError();
 }
+
 hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2,
                       hipStream_t st) {
-  return a.f32 ? dw2_t<float>(a, As, dO, dW2, st) : dw2_t<bf16_t>(a, As, dO, dW2, st);
+  if (a.f32) {
+    if (a.n % 128 == 0) dw2_launch<TileCfg<float, 128, 128, 2, 2, 3>>(a, As, dO, dW2, st);
+    else dw2_launch<TileCfg<float, 64, 128, 2, 2, 3>>(a, As, dO, dW2, st);
+  } else if (a.n % 256 == 0 && a.d % 256 == 0) {
+    dw2_launch<GradSquare>(a, As, dO, dW2, st);
+  } else if (a.n % 128 == 0 && a.d % 256 == 0) {
+    dw2_launch<GradTall>(a, As, dO, dW2, st);
+  } else if (a.n % 128 == 0) {
+    dw2_launch<GradSmall>(a, As, dO, dW2, st);
+  } else {
+    dw2_launch<TileCfg<bf16_t, 64, 128, 2, 2, 3>>(a, As, dO, dW2, st);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -13,24 +13,23 @@
 // capacity-sized grid exit at once.
 #include "gemm.hpp"
 #include "internal.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kStages = 3;
-
 // One workgroup computes a 128-row M tile against BN/2 gate columns and the
 // matching BN/2 up columns, so SiLU(gate) * up is formed in registers.
 // A = gathered X rows (K-major), B = W1_e columns (MN-major).
-template <class T, int BN>
-__global__ __launch_bounds__(256) void k_up_swiglu(
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
     const T* __restrict__ X, const T* __restrict__ W1, T* __restrict__ H, T* __restrict__ Aact,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
     const int32_t* __restrict__ totals, int d, int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages, true>;
+  static_assert(Cfg::PAIRED && Cfg::BM == kTileM, "paired 128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
-  constexpr int HALF = BN / 2, EPC = 16 / int(sizeof(T));
+  constexpr int BN = Cfg::BN, HALF = BN / 2, EPC = 16 / int(sizeof(T));
   const int NT = n / HALF;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
@@ -83,15 +82,15 @@ __global__ __launch_bounds__(256) void k_up_swiglu(
 }
 
 // A = activation rows (K-major), B = W2_e columns (MN-major).
-template <class T, int BN>
-__global__ __launch_bounds__(256) void k_down(
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_down(
     const T* __restrict__ Aact, const T* __restrict__ W2, T* __restrict__ Y,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
     int n) {
-  using Cfg = TileCfg<T, kTileM, BN, 2, 2, kStages>;
+  static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
-  constexpr int EPC = 16 / int(sizeof(T));
+  constexpr int BN = Cfg::BN, EPC = 16 / int(sizeof(T));
   const int NT = d / BN;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
@@ -131,52 +130,45 @@ __global__ __launch_bounds__(256) void k_down(
 
 inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
 
-template <class T>
-hipError_t up_t(const LayerArgs& a, const void* X, const void* W1, void* H, void* Aact,
-                hipStream_t st) {
-  const T* x = static_cast<const T*>(X);
-  const T* w = static_cast<const T*>(W1);
-  T* h = static_cast<T*>(H);
-  T* av = static_cast<T*>(Aact);
-  if (sizeof(T) == 2 && a.n % 128 == 0) {
-    hipLaunchKernelGGL((k_up_swiglu<T, 256>), dim3(grid_for(a.tile_cap * (a.n / 128))), dim3(256),
-                       0, st, x, w, h, av, a.tile_expert, a.tile_row, a.expert_offsets,
-                       a.slot_token, a.totals, a.d, a.n);
-  } else {
-    hipLaunchKernelGGL((k_up_swiglu<T, 128>), dim3(grid_for(a.tile_cap * (a.n / 64))), dim3(256),
-                       0, st, x, w, h, av, a.tile_expert, a.tile_row, a.expert_offsets,
-                       a.slot_token, a.totals, a.d, a.n);
-  }
-  return hipGetLastError();
+template <class Cfg>
+void up_launch(const LayerArgs& a, const void* X, const void* W1, void* H, void* Aact,
+               hipStream_t st) {
+  using T = typename Cfg::T;
+  const int half = Cfg::BN / 2;
+  hipLaunchKernelGGL((k_up_swiglu<Cfg>), dim3(grid_for(a.tile_cap * (a.n / half))),
+                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
+                     static_cast<const T*>(W1), static_cast<T*>(H), static_cast<T*>(Aact),
+                     a.tile_expert, a.tile_row, a.expert_offsets, a.slot_token, a.totals, a.d,
+                     a.n);
 }
 
-template <class T>
-hipError_t down_t(const LayerArgs& a, const void* Aact, const void* W2, void* Y, hipStream_t st) {
-  const T* av = static_cast<const T*>(Aact);
-  const T* w = static_cast<const T*>(W2);
-  T* y = static_cast<T*>(Y);
-  if (sizeof(T) == 2 && a.d % 256 == 0) {
-    hipLaunchKernelGGL((k_down<T, 256>), dim3(grid_for(a.tile_cap * (a.d / 256))), dim3(256), 0,
-                       st, av, w, y, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
-                       a.n);
-  } else {
-    hipLaunchKernelGGL((k_down<T, 128>), dim3(grid_for(a.tile_cap * (a.d / 128))), dim3(256), 0,
-                       st, av, w, y, a.tile_expert, a.tile_row, a.expert_offsets, a.totals, a.d,
-                       a.n);
-  }
-  return hipGetLastError();
+template <class Cfg>
+void down_launch(const LayerArgs& a, const void* Aact, const void* W2, void* Y, hipStream_t st) {
+  using T = typename Cfg::T;
+  hipLaunchKernelGGL((k_down<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
+                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(Aact),
+                     static_cast<const T*>(W2), static_cast<T*>(Y), a.tile_expert, a.tile_row,
+                     a.expert_offsets, a.totals, a.d, a.n);
 }
 
 }  // namespace
 
 hipError_t launch_up_swiglu(const LayerArgs& a, const void* X, const void* W1, void* H,
                             void* Aact, hipStream_t st) {
-  return a.f32 ? up_t<float>(a, X, W1, H, Aact, st) : up_t<bf16_t>(a, X, W1, H, Aact, st);
+  if (a.f32) up_launch<TileCfg<float, kTileM, 128, 2, 2, 3, 128, true>>(a, X, W1, H, Aact, st);
+  else if (a.n % 256 == 0) up_launch<UpWide>(a, X, W1, H, Aact, st);
+  else if (a.n % 128 == 0) up_launch<UpMid>(a, X, W1, H, Aact, st);
+  else up_launch<UpNarrow>(a, X, W1, H, Aact, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_down(const LayerArgs& a, const void* Aact, const void* W2, void* Y,
                        hipStream_t st) {
-  return a.f32 ? down_t<float>(a, Aact, W2, Y, st) : down_t<bf16_t>(a, Aact, W2, Y, st);
+  if (a.f32) down_launch<TileCfg<float, kTileM, 128, 2, 2, 3>>(a, Aact, W2, Y, st);
+  else if (a.d % 512 == 0) down_launch<RowsWide>(a, Aact, W2, Y, st);
+  else if (a.d % 256 == 0) down_launch<RowsMid>(a, Aact, W2, Y, st);
+  else down_launch<RowsNarrow>(a, Aact, W2, Y, st);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -12,14 +12,15 @@
 // order on fp64 softmax probabilities (equal keys go to the lower token).
 //
 // Kernels, in launch order on one stream:
-//   route_clear   zero the per-expert counters and the token-major bitmap
-//   route_topk    per token: top-K, fp64 softmax keys for all experts,
-//                 token-choice bitmap and histogram f_e
-//   route_round   one workgroup: r_e, expert offsets, tile schedule, order
+//   route_topk    per token: top-K, fp64 softmax keys for all experts, the
+//                 token-choice bitmap (expert-major); clears the token-major
+//                 bitmap rows of its tokens
+//   route_count   per expert: f_e = popcount of its bitmap row, r_e
+//   route_scan    one workgroup: expert offsets, tile schedule, expert order
 //   route_select  per expert: token-rounding threshold (radix select on the
 //                 64-bit keys), slot list in token order, gate weights
-//   route_tscan   one workgroup: per-token slot counts -> CSR offsets
-//   route_tslots  per token: its slots in ascending expert order
+//   route_tcount  per block of tokens: number of slots
+//   route_tslots  per token: CSR offset and its slots in ascending expert order
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -59,14 +60,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
   return res;
 }
 
-__global__ void route_clear(int32_t* __restrict__ tc_counts, int E,
-                            uint32_t* __restrict__ bits_t, int64_t nbits_t) {
-  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t j = i; j < E; j += stride) tc_counts[j] = 0;
-  for (int64_t j = i; j < nbits_t; j += stride) bits_t[j] = 0u;
-}
-
 // Orders fp32 values as unsigned integers (larger float -> larger integer).
 // -0.0 is folded into +0.0 so that the two compare equal, as floats do.
 __device__ __forceinline__ uint32_t ordered_f32(float x) {
@@ -78,125 +71,128 @@ __device__ __forceinline__ float unordered_f32(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// Eight lanes per token (lane `sub` owns experts e = sub mod 8), 32 tokens per
-// block, so each block fills exactly one bitmap word per expert.
-constexpr int kTopkLanes = 8;
-constexpr int kTopkTokens = 256 / kTopkLanes;
+// Sixteen lanes per token (lane `sub` owns experts e = sub + 16 j, j < EPL),
+// 32 tokens per 512-thread block, so each block fills exactly one bitmap word
+// per expert.  The top-K is taken in K rounds: each lane offers its best
+// expert not yet taken, the 16 lanes reduce to the maximum, and the owner
+// marks it taken.  Keys are (ordered logit, ~e), so equal logits go to the
+// lower expert.
+constexpr int kTopkLanes = 16;
+constexpr int kTopkTokens = 32;
+constexpr int kTopkThreads = kTopkLanes * kTopkTokens;
 
-template <int KMAX>
-__device__ __forceinline__ void sort_bitonic_desc(uint64_t (&c)[KMAX]) {
-#pragma unroll
-  for (int j = KMAX / 2; j >= 1; j >>= 1) {
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if ((i & j) == 0) {
-        const uint64_t a = c[i], b = c[i + j];
-        c[i] = a > b ? a : b;
-        c[i + j] = a > b ? b : a;
-      }
-    }
-  }
-}
-
-template <int KMAX>
-__global__ __launch_bounds__(256) void route_topk(
+template <int EPL>
+__global__ __launch_bounds__(kTopkThreads) void route_topk(
     const float* __restrict__ logits, int T, int E, int K,
-    int32_t* __restrict__ topk_ids, int32_t* __restrict__ tc_counts,
-    uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e) {
+    int32_t* __restrict__ topk_ids,
+    uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e, uint32_t* __restrict__ bits_t) {
+  static_assert(EPL >= 1 && EPL <= 64, "experts per lane");
   __shared__ uint32_t sbits[1024];
-  __shared__ int32_t shist[1024];
   const int tid = threadIdx.x;
-  for (int i = tid; i < E; i += 256) { sbits[i] = 0u; shist[i] = 0; }
+  for (int i = tid; i < E; i += kTopkThreads) sbits[i] = 0u;
+  {
+    // this block's rows of the token-major bitmap start empty
+    const int W = (E + 31) >> 5;
+    const int64_t beg = int64_t(blockIdx.x) * kTopkTokens * W;
+    const int64_t end = min(int64_t(T), int64_t(blockIdx.x + 1) * kTopkTokens) * W;
+    for (int64_t i = beg + tid; i < end; i += kTopkThreads) bits_t[i] = 0u;
+  }
   __syncthreads();
 
   const int sub = tid & (kTopkLanes - 1), tl = tid / kTopkLanes;
   const int t = blockIdx.x * kTopkTokens + tl;
   const bool valid = t < T;
   const float* row = logits + int64_t(valid ? t : 0) * E;
-  // key = ordered(logit) : (~e), so equal logits rank the lower expert first.
-  uint64_t best[KMAX];
+  uint32_t ok[EPL];  // ordered logits of this lane's experts (0: none)
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) best[i] = 0ull;
-  if (valid) {
-    for (int e = sub; e < E; e += kTopkLanes) {
-      const uint64_t key = (uint64_t(ordered_f32(row[e])) << 32) | uint64_t(0xffffffffu - uint32_t(e));
-      if (key > best[KMAX - 1]) {
+  for (int j = 0; j < EPL; ++j) {
+    const int e = sub + kTopkLanes * j;
+    ok[j] = (valid && e < E) ? ordered_f32(row[e]) : 0u;
+  }
+  uint64_t taken = 0ull;
+  double m = 0.0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = 0ull;
 #pragma unroll
-        for (int i = KMAX - 1; i > 0; --i) {
-          if (key > best[i - 1]) best[i] = best[i - 1];
-          else if (key > best[i]) best[i] = key;
-        }
-        if (key > best[0]) best[0] = key;
-      }
+    for (int j = 0; j < EPL; ++j) {
+      const uint32_t e = uint32_t(sub + kTopkLanes * j);
+      const uint64_t key = ((taken >> j) & 1ull) ? 0ull
+                                                 : ((uint64_t(ok[j]) << 32) | (0xffffffffu - e));
+      best = key > best ? key : best;
+    }
+#pragma unroll
+    for (int o = 1; o < kTopkLanes; o <<= 1) {
+      const uint64_t other = __shfl_xor(best, o, 64);
+      best = other > best ? other : best;
+    }
+    const int eb = int(0xffffffffu - uint32_t(best));
+    if (k == 0) m = double(unordered_f32(uint32_t(best >> 32)));
+    if ((eb & (kTopkLanes - 1)) == sub) taken |= 1ull << (eb / kTopkLanes);
+    if (valid && (k & (kTopkLanes - 1)) == sub) {
+      topk_ids[int64_t(t) * K + k] = eb;
+      atomicOr(&sbits[eb], 1u << tl);
     }
   }
-  // Merge the eight partial lists (disjoint expert sets) with bitonic merges.
-#pragma unroll
-  for (int o = 1; o < kTopkLanes; o <<= 1) {
-    uint64_t c[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      const uint64_t other = __shfl_xor(best[KMAX - 1 - i], o, 64);
-      c[i] = best[i] > other ? best[i] : other;
-    }
-    sort_bitonic_desc<KMAX>(c);
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) best[i] = c[i];
-  }
-  const double m = double(unordered_f32(uint32_t(best[0] >> 32)));
   double z = 0.0;
-  if (valid)
-    for (int e = sub; e < E; e += kTopkLanes) z += exp(double(row[e]) - m);
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = sub + kTopkLanes * j;
+      if (e < E) z += exp(double(row[e]) - m);
+    }
+  }
 #pragma unroll
   for (int o = 1; o < kTopkLanes; o <<= 1) z += __shfl_xor(z, o, 64);
-  int ids[KMAX];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) ids[i] = int(0xffffffffu - uint32_t(best[i]));
   if (valid) {
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if (i < K && (i % kTopkLanes) == sub) {
-        topk_ids[int64_t(t) * K + i] = ids[i];
-        atomicAdd(&shist[ids[i]], 1);
-        atomicOr(&sbits[ids[i]], 1u << tl);
+    for (int j = 0; j < EPL; ++j) {
+      const int e = sub + kTopkLanes * j;
+      if (e < E) {
+        const double p = exp(double(row[e]) - m) / z;
+        keys[int64_t(e) * T + t] =
+            (((taken >> j) & 1ull) << 63) | uint64_t(__double_as_longlong(p));
       }
-    }
-    for (int e = sub; e < E; e += kTopkLanes) {
-      const double p = exp(double(row[e]) - m) / z;
-      bool tc = false;
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) tc |= (i < K) && (ids[i] == e);
-      keys[int64_t(e) * T + t] = (uint64_t(tc) << 63) | uint64_t(__double_as_longlong(p));
     }
   }
   __syncthreads();
   const int nw = (T + 31) >> 5;
-  for (int e = tid; e < E; e += 256) {
-    bits_e[int64_t(e) * nw + blockIdx.x] = sbits[e];
-    if (shist[e]) atomicAdd(&tc_counts[e], shist[e]);
-  }
+  for (int e = tid; e < E; e += kTopkThreads) bits_e[int64_t(e) * nw + blockIdx.x] = sbits[e];
 }
 
-// One workgroup of 1024 threads, one expert per thread (E <= 1024).
-__global__ __launch_bounds__(kScanThreads) void route_round(
-    const int32_t* __restrict__ tc_counts, int E, int T, int M, int mode,
-    int32_t* __restrict__ counts, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ expert_order, int32_t* __restrict__ tile_expert,
-    int32_t* __restrict__ tile_row, int32_t* __restrict__ totals) {
-  __shared__ int sh[kScanThreads / 64 + 1];
-  __shared__ int sr[1024];
-  const int e = threadIdx.x;
-  int r = 0;
-  if (e < E) {
-    const int f = tc_counts[e];
-    r = f;
+// Per expert: f_e = number of set bits in its row of the token-choice bitmap,
+// and the rounded count r_e.
+__global__ __launch_bounds__(256) void route_count(
+    int T, int M, int mode, const uint32_t* __restrict__ bits_e, int32_t* __restrict__ tc_counts,
+    int32_t* __restrict__ counts) {
+  __shared__ int sh[256 / 64 + 1];
+  const int e = blockIdx.x, nw = (T + 31) >> 5;
+  const uint32_t* row = bits_e + int64_t(e) * nw;
+  int c = 0;
+  for (int w = threadIdx.x; w < nw; w += 256) c += __popc(row[w]);
+  int f;
+  block_excl_scan(c, sh, &f);
+  if (threadIdx.x == 0) {
+    int r = f;
     if (mode == 1) {
       const int lo = (f / M) * M;
       const int hi = (f % M == 0) ? f : lo + M;
       r = ((hi - f) < (f - lo) && hi <= T) ? hi : lo;
     }
+    tc_counts[e] = f;
     counts[e] = r;
   }
+}
+
+// One workgroup of 1024 threads, one expert per thread (E <= 1024): slot
+// offsets, the M-tile schedule and the experts ordered by descending count.
+__global__ __launch_bounds__(kScanThreads) void route_scan(
+    const int32_t* __restrict__ counts, int E, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ expert_order, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ tile_row, int32_t* __restrict__ totals) {
+  __shared__ int sh[kScanThreads / 64 + 1];
+  __shared__ int sr[1024];
+  const int e = threadIdx.x;
+  const int r = e < E ? counts[e] : 0;
   sr[e] = r;
   int S, ntiles;
   const int off = block_excl_scan(r, sh, &S);
@@ -225,13 +221,20 @@ __global__ __launch_bounds__(kScanThreads) void route_round(
 
 // Per expert: keep the r_e best tokens under the key (is-TC, p) descending,
 // equal keys to the lower token, then list them in token order as slots.
+// With LDS_KEYS the expert's T keys are copied to LDS once (T <= 16384) and
+// the eight radix passes read them there instead of from L2.
+constexpr int kLdsKeys = 16384;
+template <bool LDS_KEYS>
 __global__ __launch_bounds__(kSelectThreads) void route_select(
     int T, int E, const int32_t* __restrict__ tc_counts,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ expert_offsets,
     const uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e,
     uint32_t* __restrict__ bits_t, int32_t* __restrict__ wbase,
     int32_t* __restrict__ slot_token, float* __restrict__ slot_weight) {
-  __shared__ uint32_t hist[16][256];
+  __shared__ uint64_t skeys[LDS_KEYS ? kLdsKeys : 1];
+  // 16 copies of the 256-bin histogram; the +1 pad puts the copies of one
+  // digit in 16 different banks
+  __shared__ uint32_t hist[16][257];
   __shared__ uint32_t tot[256];
   __shared__ int sh[kSelectThreads / 64 + 1];
   __shared__ uint64_t s_digit_info[3];
@@ -246,14 +249,42 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
     uint64_t prefix = 0ull, mask = 0ull;
     int rem = r;  // rank (from the top, 1-based) still to locate under prefix
     uint32_t cnt_eq = 0;
+    const uint64_t* kp = ke;
+    if (LDS_KEYS && r > 0) {
+      if ((T & 1) == 0) {
+        // rows of an even T start 16-byte aligned: copy two keys per load
+        const uint4* src = reinterpret_cast<const uint4*>(ke);
+        uint4* dst = reinterpret_cast<uint4*>(skeys);
+#pragma unroll 8
+        for (int i = tid; i < T / 2; i += kSelectThreads) dst[i] = src[i];
+      } else {
+#pragma unroll 8
+        for (int t = tid; t < T; t += kSelectThreads) skeys[t] = ke[t];
+      }
+      __syncthreads();
+      kp = skeys;
+    }
     if (r > 0) {
       for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;
-        for (int i = tid; i < 16 * 256; i += kSelectThreads) (&hist[0][0])[i] = 0u;
+        for (int i = tid; i < 16 * 257; i += kSelectThreads) (&hist[0][0])[i] = 0u;
         __syncthreads();
-        for (int t = tid; t < T; t += kSelectThreads) {
-          const uint64_t k = ke[t];
-          if ((k & mask) == prefix) atomicAdd(&hist[tid & 15][(k >> shift) & 255u], 1u);
+        // Wave-uniform trip count, so the ballots below see whole waves.
+        for (int t0 = 0; t0 < T; t0 += kSelectThreads) {
+          const int t = t0 + tid;
+          const uint64_t k = t < T ? kp[t] : 0ull;
+          const bool match = t < T && (k & mask) == prefix;
+          const uint32_t dg = uint32_t(k >> shift) & 255u;
+          // early passes see one digit across the wave: add it once
+          const uint64_t all = __ballot(match);
+          const int lead = all ? __ffsll((unsigned long long)all) - 1 : 0;
+          const uint32_t d0 = __shfl(dg, lead, 64);
+          const uint64_t same = __ballot(match && dg == d0);
+          if (all != 0ull && all == same) {
+            if ((tid & 63) == lead) atomicAdd(&hist[0][d0], uint32_t(__popcll(all)));
+          } else if (match) {
+            atomicAdd(&hist[tid & 15][dg], 1u);
+          }
         }
         __syncthreads();
         {
@@ -302,7 +333,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
         for (int b = 0; b < 32; ++b) {
           const int t = w * 32 + b;
           if (t < T) {
-            const uint64_t k = ke[t];
+            const uint64_t k = kp[t];
             if (k > prefix || (all_eq && k == prefix)) word |= 1u << b;
           }
         }
@@ -314,7 +345,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
       int taken = 0;
       for (int base = 0; base < T; base += kSelectThreads) {
         const int t = base + tid;
-        const int flag = (t < T) && (ke[t] == prefix);
+        const int flag = (t < T) && (kp[t] == prefix);
         int chunk;
         const int ex = block_excl_scan(flag, sh, &chunk);
         if (flag && taken + ex < rem) atomicOr(&be[t >> 5], 1u << (t & 31));
@@ -324,7 +355,8 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
     }
   }
 
-  // Compaction in token order.
+  // Compaction in token order: the word pass lists the kept tokens; a flat
+  // pass over the expert's slots then fetches all gate weights in parallel.
   const int off = expert_offsets[e];
   int carry = 0;
   for (int base = 0; base < nw; base += kSelectThreads) {
@@ -341,45 +373,61 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
       while (m && wb + i < r) {
         const int b = __ffs(m) - 1;
         m &= m - 1;
-        const int t = w * 32 + b;
-        const int slot = off + wb + i++;
-        slot_token[slot] = t;
-        const uint64_t k = ke[t] & 0x7fffffffffffffffull;
-        slot_weight[slot] = float(__longlong_as_double(int64_t(k)));
-        atomicOr(&bits_t[int64_t(t) * W + (e >> 5)], 1u << (e & 31));
+        slot_token[off + wb + i++] = w * 32 + b;
       }
     }
     carry += chunk;
   }
-}
-
-__global__ __launch_bounds__(kScanThreads) void route_tscan(
-    int T, int E, const uint32_t* __restrict__ bits_t, int32_t* __restrict__ token_offsets) {
-  __shared__ int sh[kScanThreads / 64 + 1];
-  const int W = (E + 31) >> 5;
-  int carry = 0;
-  for (int base = 0; base < T; base += kScanThreads) {
-    const int t = base + threadIdx.x;
-    int c = 0;
-    if (t < T)
-      for (int w = 0; w < W; ++w) c += __popc(bits_t[int64_t(t) * W + w]);
-    int chunk;
-    const int ex = block_excl_scan(c, sh, &chunk);
-    if (t < T) token_offsets[t] = carry + ex;
-    carry += chunk;
+  __syncthreads();
+  const int kept = min(carry, r);
+#pragma unroll 4
+  for (int i = tid; i < kept; i += kSelectThreads) {
+    const int t = slot_token[off + i];
+    const uint64_t k = ke[t] & 0x7fffffffffffffffull;
+    slot_weight[off + i] = float(__longlong_as_double(int64_t(k)));
+    atomicOr(&bits_t[int64_t(t) * W + (e >> 5)], 1u << (e & 31));
   }
-  if (threadIdx.x == 0) token_offsets[T] = carry;
 }
 
+// Per block of 256 tokens: the number of slots of those tokens.
+__global__ __launch_bounds__(256) void route_tcount(int T, int E,
+                                                    const uint32_t* __restrict__ bits_t,
+                                                    int32_t* __restrict__ block_sum) {
+  __shared__ int sh[256 / 64 + 1];
+  const int W = (E + 31) >> 5, t = blockIdx.x * 256 + threadIdx.x;
+  int c = 0;
+  if (t < T)
+    for (int w = 0; w < W; ++w) c += __popc(bits_t[int64_t(t) * W + w]);
+  int total;
+  block_excl_scan(c, sh, &total);
+  if (threadIdx.x == 0) block_sum[blockIdx.x] = total;
+}
+
+// Per token: CSR offset (earlier blocks' sums + exclusive scan inside the
+// block) and the token's slots in ascending expert order.
 __global__ __launch_bounds__(256) void route_tslots(
     int T, int E, const uint32_t* __restrict__ bits_t, const uint32_t* __restrict__ bits_e,
     const int32_t* __restrict__ wbase, const int32_t* __restrict__ expert_offsets,
-    const int32_t* __restrict__ token_offsets, int32_t* __restrict__ token_slots) {
+    const int32_t* __restrict__ block_sum, int32_t* __restrict__ token_offsets,
+    int32_t* __restrict__ token_slots) {
+  __shared__ int sh[256 / 64 + 1];
+  const int W = (E + 31) >> 5, nw = (T + 31) >> 5;
   const int t = blockIdx.x * 256 + threadIdx.x;
+  int before = 0;
+  for (int b = threadIdx.x; b < int(blockIdx.x); b += 256) before += block_sum[b];
+  int base;
+  block_excl_scan(before, sh, &base);  // base = sum over all earlier blocks
+  int c = 0;
+  if (t < T)
+    for (int w = 0; w < W; ++w) c += __popc(bits_t[int64_t(t) * W + w]);
+  int total;
+  const int j0 = base + block_excl_scan(c, sh, &total);
+  if (t < T) token_offsets[t] = j0;
+  if (t == T - 1) token_offsets[T] = j0 + c;
   if (t >= T) return;
-  const int W = (E + 31) >> 5, nw = (T + 31) >> 5, tw = t >> 5;
+  const int tw = t >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
-  int j = token_offsets[t];
+  int j = j0;
   for (int w = 0; w < W; ++w) {
     uint32_t m = bits_t[int64_t(t) * W + w];
     while (m) {
@@ -401,44 +449,45 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
   uint32_t* bits_e = reinterpret_cast<uint32_t*>(ws + L.bits_e);
   uint32_t* bits_t = reinterpret_cast<uint32_t*>(ws + L.bits_t);
   int32_t* wbase = reinterpret_cast<int32_t*>(ws + L.wbase);
-  const int W = (E + 31) / 32;
-  const int64_t nbits_t = int64_t(T) * W;
+  int32_t* block_sum = reinterpret_cast<int32_t*>(ws + L.block_sum);
 
   tr.mark(st, 0);
   {
-    const int blocks = int(std::min<int64_t>(1024, cdiv<int64_t>(std::max<int64_t>(nbits_t, E), 256)));
-    hipLaunchKernelGGL(route_clear, dim3(blocks), dim3(256), 0, st, a.tc_counts, E, bits_t, nbits_t);
+    const dim3 grid(cdiv(T, kTopkTokens));
+    const int epl = (E + kTopkLanes - 1) / kTopkLanes;
+#define MOE_TOPK(N)                                                                        \
+  hipLaunchKernelGGL(route_topk<N>, grid, dim3(kTopkThreads), 0, st, a.logits, T, E, K,  \
+                     a.topk_ids, keys, bits_e, bits_t)
+    if (epl <= 1) MOE_TOPK(1);
+    else if (epl <= 2) MOE_TOPK(2);
+    else if (epl <= 4) MOE_TOPK(4);
+    else if (epl <= 8) MOE_TOPK(8);
+    else if (epl <= 16) MOE_TOPK(16);
+    else if (epl <= 32) MOE_TOPK(32);
+    else MOE_TOPK(64);
+#undef MOE_TOPK
   }
   tr.mark(st, 1);
-  {
-    const dim3 grid(cdiv(T, kTopkTokens));
-    if (K <= 2)
-      hipLaunchKernelGGL(route_topk<2>, grid, dim3(256), 0, st, a.logits, T, E, K, a.topk_ids,
-                         a.tc_counts, keys, bits_e);
-    else if (K <= 8)
-      hipLaunchKernelGGL(route_topk<8>, grid, dim3(256), 0, st, a.logits, T, E, K, a.topk_ids,
-                         a.tc_counts, keys, bits_e);
-    else if (K <= 16)
-      hipLaunchKernelGGL(route_topk<16>, grid, dim3(256), 0, st, a.logits, T, E, K, a.topk_ids,
-                         a.tc_counts, keys, bits_e);
-    else
-      hipLaunchKernelGGL(route_topk<32>, grid, dim3(256), 0, st, a.logits, T, E, K, a.topk_ids,
-                         a.tc_counts, keys, bits_e);
-  }
+  hipLaunchKernelGGL(route_count, dim3(E), dim3(256), 0, st, T, a.M, a.mode, bits_e, a.tc_counts,
+                     a.counts);
   tr.mark(st, 2);
-  hipLaunchKernelGGL(route_round, dim3(1), dim3(kScanThreads), 0, st, a.tc_counts, E, T, a.M,
-                     a.mode, a.counts, a.expert_offsets, a.expert_order, a.tile_expert,
-                     a.tile_row, a.totals);
+  hipLaunchKernelGGL(route_scan, dim3(1), dim3(kScanThreads), 0, st, a.counts, E,
+                     a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row, a.totals);
   tr.mark(st, 3);
-  hipLaunchKernelGGL(route_select, dim3(E), dim3(kSelectThreads), 0, st, T, E, a.tc_counts,
-                     a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
-                     a.slot_weight);
+  if (T <= kLdsKeys)
+    hipLaunchKernelGGL(route_select<true>, dim3(E), dim3(kSelectThreads), 0, st, T, E,
+                       a.tc_counts, a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase,
+                       a.slot_token, a.slot_weight);
+  else
+    hipLaunchKernelGGL(route_select<false>, dim3(E), dim3(kSelectThreads), 0, st, T, E,
+                       a.tc_counts, a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase,
+                       a.slot_token, a.slot_weight);
   tr.mark(st, 4);
-  hipLaunchKernelGGL(route_tscan, dim3(1), dim3(kScanThreads), 0, st, T, E, bits_t,
-                     a.token_offsets);
+  const dim3 tgrid(cdiv(T, 256));
+  hipLaunchKernelGGL(route_tcount, tgrid, dim3(256), 0, st, T, E, bits_t, block_sum);
   tr.mark(st, 5);
-  hipLaunchKernelGGL(route_tslots, dim3(cdiv(T, 256)), dim3(256), 0, st, T, E, bits_t, bits_e,
-                     wbase, a.expert_offsets, a.token_offsets, a.token_slots);
+  hipLaunchKernelGGL(route_tslots, tgrid, dim3(256), 0, st, T, E, bits_t, bits_e, wbase,
+                     a.expert_offsets, block_sum, a.token_offsets, a.token_slots);
   tr.mark(st, 6);
   return hipGetLastError();
 }

@@ -14,13 +14,14 @@ from dataclasses import dataclass, field
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# In-tree build; MOE_LIBRARY may name another build of the same library.
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 MOE_BF16, MOE_F32 = 0, 1
 MOE_ROUTE_TC, MOE_ROUTE_TR = 0, 1
 TILE_M = 128
 
-ROUTE_KERNELS = ("route_clear", "route_topk", "route_round", "route_select", "route_tscan",
+ROUTE_KERNELS = ("route_topk", "route_count", "route_scan", "route_select", "route_tcount",
                  "route_tslots")
 FWD_KERNELS = ("up_swiglu", "down", "aggregate_O")
 BWD_KERNELS = ("dh", "dxt", "aggregate_dX", "dw1", "dw2")
