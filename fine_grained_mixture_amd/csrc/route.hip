@@ -27,7 +27,6 @@
 namespace moe {
 namespace {
 
-constexpr int kSelectThreads = 256;
 constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -221,24 +220,27 @@ __global__ __launch_bounds__(kScanThreads) void route_scan(
 
 // Per expert: keep the r_e best tokens under the key (is-TC, p) descending,
 // equal keys to the lower token, then list them in token order as slots.
-// With LDS_KEYS the expert's T keys are copied to LDS once (T <= 16384) and
-// the eight radix passes read them there instead of from L2.
-constexpr int kLdsKeys = 16384;
-template <bool LDS_KEYS>
-__global__ __launch_bounds__(kSelectThreads) void route_select(
+//
+// With KPT > 0 each of the 1024 threads holds the keys of tokens
+// t = j * 1024 + tid (j < KPT) in registers, so the eight 8-bit radix passes
+// need no memory traffic; KPT == 0 reads the keys from memory in every pass
+// (any T).
+constexpr int kSelThreads = 1024;
+
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void route_select(
     int T, int E, const int32_t* __restrict__ tc_counts,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ expert_offsets,
     const uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e,
     uint32_t* __restrict__ bits_t, int32_t* __restrict__ wbase,
     int32_t* __restrict__ slot_token, float* __restrict__ slot_weight) {
-  __shared__ uint64_t skeys[LDS_KEYS ? kLdsKeys : 1];
   // 16 copies of the 256-bin histogram; the +1 pad puts the copies of one
   // digit in 16 different banks
   __shared__ uint32_t hist[16][257];
   __shared__ uint32_t tot[256];
-  __shared__ int sh[kSelectThreads / 64 + 1];
-  __shared__ uint64_t s_digit_info[3];
-  const int e = blockIdx.x, tid = threadIdx.x;
+  __shared__ int sh[kSelThreads / 64 + 1];
+  __shared__ int s_digit_info[3];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int f = tc_counts[e], r = counts[e];
   const int nw = (T + 31) >> 5;
   const int W = (E + 31) >> 5;
@@ -246,70 +248,58 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
   uint32_t* be = bits_e + int64_t(e) * nw;
 
   if (r != f) {
+    uint64_t kr[KPT > 0 ? KPT : 1];
+    if constexpr (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int t = j * kSelThreads + tid;
+        kr[j] = t < T ? ke[t] : 0ull;  // 0 ranks below every real key
+      }
+    }
     uint64_t prefix = 0ull, mask = 0ull;
     int rem = r;  // rank (from the top, 1-based) still to locate under prefix
-    uint32_t cnt_eq = 0;
-    const uint64_t* kp = ke;
-    if (LDS_KEYS && r > 0) {
-      if ((T & 1) == 0) {
-        // rows of an even T start 16-byte aligned: copy two keys per load
-        const uint4* src = reinterpret_cast<const uint4*>(ke);
-        uint4* dst = reinterpret_cast<uint4*>(skeys);
-#pragma unroll 8
-        for (int i = tid; i < T / 2; i += kSelectThreads) dst[i] = src[i];
-      } else {
-#pragma unroll 8
-        for (int t = tid; t < T; t += kSelectThreads) skeys[t] = ke[t];
-      }
-      __syncthreads();
-      kp = skeys;
-    }
+    int cnt_eq = 0;
     if (r > 0) {
       for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;
-        for (int i = tid; i < 16 * 257; i += kSelectThreads) (&hist[0][0])[i] = 0u;
+        for (int i = tid; i < 16 * 257; i += kSelThreads) (&hist[0][0])[i] = 0u;
         __syncthreads();
-        // Wave-uniform trip count, so the ballots below see whole waves.
-        for (int t0 = 0; t0 < T; t0 += kSelectThreads) {
-          const int t = t0 + tid;
-          const uint64_t k = t < T ? kp[t] : 0ull;
-          const bool match = t < T && (k & mask) == prefix;
-          const uint32_t dg = uint32_t(k >> shift) & 255u;
-          // early passes see one digit across the wave: add it once
-          const uint64_t all = __ballot(match);
-          const int lead = all ? __ffsll((unsigned long long)all) - 1 : 0;
-          const uint32_t d0 = __shfl(dg, lead, 64);
-          const uint64_t same = __ballot(match && dg == d0);
-          if (all != 0ull && all == same) {
-            if ((tid & 63) == lead) atomicAdd(&hist[0][d0], uint32_t(__popcll(all)));
-          } else if (match) {
-            atomicAdd(&hist[tid & 15][dg], 1u);
+        uint32_t* hc = hist[tid & 15];
+        if constexpr (KPT > 0) {
+#pragma unroll
+          for (int j = 0; j < KPT; ++j) {
+            const int t = j * kSelThreads + tid;
+            if (t < T && (kr[j] & mask) == prefix) atomicAdd(&hc[(kr[j] >> shift) & 255u], 1u);
+          }
+        } else {
+          for (int t = tid; t < T; t += kSelThreads) {
+            const uint64_t k = ke[t];
+            if ((k & mask) == prefix) atomicAdd(&hc[(k >> shift) & 255u], 1u);
           }
         }
         __syncthreads();
-        {
-          uint32_t s = 0;
+        if (tid < 256) {
+          uint32_t c = 0;
 #pragma unroll
-          for (int c = 0; c < 16; ++c) s += hist[c][tid];
-          tot[tid] = s;
+          for (int q = 0; q < 16; ++q) c += hist[q][tid];
+          tot[tid] = c;
         }
         __syncthreads();
         if (tid < 64) {
           // lane l covers digits 255-4l .. 252-4l (descending)
           uint32_t c[4];
-          int s = 0;
+          int sum = 0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { c[j] = tot[255 - 4 * tid - j]; s += int(c[j]); }
-          const int incl = wave_incl_scan(s);
-          int excl = incl - s;
-          const bool hit = (excl < rem) && (rem <= incl);
-          if (hit) {
+          for (int j = 0; j < 4; ++j) { c[j] = tot[255 - 4 * tid - j]; sum += int(c[j]); }
+          const int incl = wave_incl_scan(sum);
+          int excl = incl - sum;
+          if (excl < rem && rem <= incl) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               if (excl + int(c[j]) >= rem) {
-                s_digit_info[0] = uint64_t(255 - 4 * tid - j);
-                s_digit_info[1] = uint64_t(rem - excl);
-                s_digit_info[2] = uint64_t(c[j]);
+                s_digit_info[0] = 255 - 4 * tid - j;
+                s_digit_info[1] = rem - excl;
+                s_digit_info[2] = int(c[j]);
                 break;
               }
               excl += int(c[j]);
@@ -317,35 +307,49 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
           }
         }
         __syncthreads();
-        prefix |= s_digit_info[0] << shift;
+        prefix |= uint64_t(uint32_t(s_digit_info[0])) << shift;
         mask |= 0xffull << shift;
-        rem = int(s_digit_info[1]);
-        cnt_eq = uint32_t(s_digit_info[2]);
+        rem = s_digit_info[1];
+        cnt_eq = s_digit_info[2];
         __syncthreads();
       }
     }
     // prefix is now the r-th largest key; `rem` of the cnt_eq equal keys are
     // kept, the lowest tokens first.
-    const bool all_eq = (r > 0) && (int(cnt_eq) == rem);
-    for (int w = tid; w < nw; w += kSelectThreads) {
-      uint32_t word = 0u;
-      if (r > 0) {
-        for (int b = 0; b < 32; ++b) {
-          const int t = w * 32 + b;
-          if (t < T) {
-            const uint64_t k = kp[t];
-            if (k > prefix || (all_eq && k == prefix)) word |= 1u << b;
+    const bool all_eq = (r > 0) && (cnt_eq == rem);
+    if constexpr (KPT > 0) {
+      // one ballot covers 64 consecutive tokens = two bitmap words
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int t = j * kSelThreads + tid;
+        const bool keep = r > 0 && t < T && (kr[j] > prefix || (all_eq && kr[j] == prefix));
+        const uint64_t m = __ballot(keep);
+        const int w0 = t >> 5;  // even: lane 0 starts a word
+        if (lane == 0 && w0 < nw) be[w0] = uint32_t(m);
+        if (lane == 32 && w0 < nw) be[w0] = uint32_t(m >> 32);
+      }
+    } else {
+      for (int w = tid; w < nw; w += kSelThreads) {
+        uint32_t word = 0u;
+        if (r > 0) {
+          for (int b = 0; b < 32; ++b) {
+            const int t = w * 32 + b;
+            if (t < T) {
+              const uint64_t k = ke[t];
+              if (k > prefix || (all_eq && k == prefix)) word |= 1u << b;
+            }
           }
         }
+        be[w] = word;
       }
-      be[w] = word;
     }
     __syncthreads();
     if (r > 0 && !all_eq) {
+      // several tokens share the boundary key: keep the lowest `rem` of them
       int taken = 0;
-      for (int base = 0; base < T; base += kSelectThreads) {
+      for (int base = 0; base < T; base += kSelThreads) {
         const int t = base + tid;
-        const int flag = (t < T) && (kp[t] == prefix);
+        const int flag = (t < T) && (ke[t] == prefix);
         int chunk;
         const int ex = block_excl_scan(flag, sh, &chunk);
         if (flag && taken + ex < rem) atomicOr(&be[t >> 5], 1u << (t & 31));
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
   // pass over the expert's slots then fetches all gate weights in parallel.
   const int off = expert_offsets[e];
   int carry = 0;
-  for (int base = 0; base < nw; base += kSelectThreads) {
+  for (int base = 0; base < nw; base += kSelThreads) {
     const int w = base + tid;
     const uint32_t word = (w < nw) ? be[w] : 0u;
     int chunk;
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select(
   __syncthreads();
   const int kept = min(carry, r);
 #pragma unroll 4
-  for (int i = tid; i < kept; i += kSelectThreads) {
+  for (int i = tid; i < kept; i += kSelThreads) {
     const int t = slot_token[off + i];
     const uint64_t k = ke[t] & 0x7fffffffffffffffull;
     slot_weight[off + i] = float(__longlong_as_double(int64_t(k)));
@@ -474,14 +478,22 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(kScanThreads), 0, st, a.counts, E,
                      a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row, a.totals);
   tr.mark(st, 3);
-  if (T <= kLdsKeys)
-    hipLaunchKernelGGL(route_select<true>, dim3(E), dim3(kSelectThreads), 0, st, T, E,
-                       a.tc_counts, a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase,
-                       a.slot_token, a.slot_weight);
+  if (T <= 8 * kSelThreads)
+    hipLaunchKernelGGL(route_select<8>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
+                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
+                       a.slot_weight);
+  else if (T <= 16 * kSelThreads)
+    hipLaunchKernelGGL(route_select<16>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
+                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
+                       a.slot_weight);
+  else if (T <= 32 * kSelThreads)
+    hipLaunchKernelGGL(route_select<32>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
+                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
+                       a.slot_weight);
   else
-    hipLaunchKernelGGL(route_select<false>, dim3(E), dim3(kSelectThreads), 0, st, T, E,
-                       a.tc_counts, a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase,
-                       a.slot_token, a.slot_weight);
+    hipLaunchKernelGGL(route_select<0>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
+                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
+                       a.slot_weight);
   tr.mark(st, 4);
   const dim3 tgrid(cdiv(T, 256));
   hipLaunchKernelGGL(route_tcount, tgrid, dim3(256), 0, st, T, E, bits_t, block_sum);
