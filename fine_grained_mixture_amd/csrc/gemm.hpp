@@ -428,6 +428,71 @@ struct NoTail {
   __device__ __forceinline__ void operator()(int, char*) const {}
 };
 
+// Epilogue staging.  A wave deposits the values of one 32-row accumulator
+// block (lane l: row l % 32, four consecutive columns per MFMA group) into a
+// wave-private LDS buffer, then writes whole rows to global memory with
+// 16-byte stores, so each store instruction covers several full 128-byte
+// lines instead of 32 partial ones.  Rows are padded by 8 bytes so that the
+// 32 rows written at one column fall in distinct banks.
+template <class T, int COLS>
+struct RowStage {
+  static constexpr int RB = COLS * int(sizeof(T));
+  static_assert(RB % 16 == 0, "whole 16-byte chunks per row");
+  static constexpr int LDR = RB + 8;
+  static constexpr int BYTES = 32 * LDR;
+  char* buf;
+
+  __device__ __forceinline__ void put(int row, int col, const T (&v)[4]) const {
+    __builtin_memcpy(buf + row * LDR + col * int(sizeof(T)), v, sizeof(v));
+  }
+  // rowptr(r): destination of staged column 0 of block row r, or nullptr.
+  template <class RowPtr>
+  __device__ __forceinline__ void flush(RowPtr rowptr) const {
+    constexpr int CPR = RB / 16;
+    const int lane = threadIdx.x & 63;
+    asm volatile("" ::: "memory");  // deposits before read-back (LDS keeps wave order)
+#pragma unroll
+    for (int idx = lane; idx < 32 * CPR; idx += 64) {
+      const int r = idx / CPR, c = idx % CPR;
+      const char* src = buf + r * LDR + c * 16;
+      const uint2 lo = *reinterpret_cast<const uint2*>(src);
+      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+      T* g = rowptr(r);
+      if (g) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(g) + c * 16) =
+          make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    asm volatile("" ::: "memory");  // read-back before the next deposits
+  }
+};
+
+// Writes a plain accumulator tile: wave block rows go to rowptr(tile_row) +
+// (wave's first column), via the staging buffer at lds + wave * BYTES.
+template <class Cfg, class RowPtr>
+__device__ __forceinline__ void store_acc_staged(const Accum<Cfg>& acc, char* lds, RowPtr rowptr) {
+  using T = typename Cfg::T;
+  using St = RowStage<T, Cfg::WTN>;
+  const St st{lds + wave_id() * St::BYTES};
+  const int r32 = acc.lane & 31, h = acc.lane >> 5;
+  const int c0 = Cfg::colblock(acc.wn, 0);
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a) {
+#pragma unroll
+    for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        T v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
+        st.put(r32, b * 32 + q * 8 + h * 4, v);
+      }
+    const int rb = acc.wm * Cfg::WTM + a * 32;
+    st.flush([&](int r) -> T* {
+      T* row = rowptr(rb + r);
+      return row ? row + c0 : nullptr;
+    });
+  }
+}
+
 // Spreads `work` logical tiles over the 8 XCDs in contiguous chunks:
 // workgroups are dispatched round-robin over XCDs, so block b runs on XCD
 // b % 8; giving each XCD a contiguous range keeps neighbouring tiles (same

@@ -54,41 +54,71 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
   acc.init();
   pipeline<Cfg, true, true>(acc, lds, d / Cfg::BK, la, lb, NoTail{});
 
-  float* red = reinterpret_cast<float*>(lds);  // [WGN][BM] partial row sums
+  // Epilogue: per row, dS = <dA', A> (A from the stored H), dH = dSwiGLU and
+  // s * A for the dW2 GEMM.  The three outputs are staged per wave and
+  // written as whole rows (through three buffers when they fit in LDS, else
+  // one after another through one), and the partial row sums of dS meet in
+  // LDS past the staging area.
+  using St = RowStage<T, Cfg::WTN>;
+  constexpr int RED = Cfg::WGN * BM * 4;
+  constexpr bool kAll = 3 * St::BYTES * Cfg::NW + RED <= Cfg::LDS_BYTES;
+  constexpr int NSB = kAll ? 3 : 1;
+  static_assert(NSB * St::BYTES * Cfg::NW + RED <= Cfg::LDS_BYTES, "staging fits");
+  char* wbuf = lds + wave_id() * NSB * St::BYTES;
+  const St stg[3] = {St{wbuf}, St{wbuf + (kAll ? St::BYTES : 0)},
+                     St{wbuf + (kAll ? 2 * St::BYTES : 0)}};
+  float* red = reinterpret_cast<float*>(lds + NSB * St::BYTES * Cfg::NW);  // [WGN][BM]
+  const int r32 = acc.lane & 31, h = acc.lane >> 5;
+  const int cw = Cfg::colblock(acc.wn, 0);  // first column of this wave
 #pragma unroll
   for (int a = 0; a < Cfg::MB; ++a) {
     const int i = acc.row(a), slot = row0 + i;
+    const bool live = slot < rend;
+    const int srow = live ? slot : row0;  // rows past the expert read a valid row
+    const float s = slot_weight[srow];
+    const T* hrow = H + int64_t(srow) * n2;
     float part = 0.0f;
-    if (slot < rend) {
-      const float s = slot_weight[slot];
-      const T* hrow = H + int64_t(slot) * n2;
-      T* dhrow = dH + int64_t(slot) * n2;
-      T* asrow = As + int64_t(slot) * n;
+    T out[3][Cfg::NB][4][4];  // dH gate, dH up, s * A
 #pragma unroll
-      for (int b = 0; b < Cfg::NB; ++b) {
+    for (int b = 0; b < Cfg::NB; ++b) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = acc.col(b, q);
-          T g4[4], u4[4], dg4[4], du4[4], as4[4];
-          __builtin_memcpy(g4, hrow + j, sizeof(g4));
-          __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
+      for (int q = 0; q < 4; ++q) {
+        const int j = acc.col(b, q);
+        T g4[4], u4[4];
+        __builtin_memcpy(g4, hrow + j, sizeof(g4));
+        __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float x = acc.acc[a][b][q * 4 + c];  // dA'
-            const float g = Elem<T>::load(g4[c]), u = Elem<T>::load(u4[c]);
-            const float sg = sigmoidf_(g), silu = g * sg;
-            const float av = silu * u;
-            part += x * av;
-            const float da = s * x;
-            dg4[c] = Elem<T>::store(da * u * sg * (1.0f + g * (1.0f - sg)));
-            du4[c] = Elem<T>::store(da * silu);
-            as4[c] = Elem<T>::store(s * av);
-          }
-          __builtin_memcpy(dhrow + j, dg4, sizeof(dg4));
-          __builtin_memcpy(dhrow + n + j, du4, sizeof(du4));
-          __builtin_memcpy(asrow + j, as4, sizeof(as4));
+        for (int c = 0; c < 4; ++c) {
+          const float x = acc.acc[a][b][q * 4 + c];  // dA'
+          const float g = Elem<T>::load(g4[c]), u = Elem<T>::load(u4[c]);
+          const float sg = sigmoidf_(g), silu = g * sg;
+          const float av = silu * u;
+          part += x * av;
+          const float da = s * x;
+          out[0][b][q][c] = Elem<T>::store(da * u * sg * (1.0f + g * (1.0f - sg)));
+          out[1][b][q][c] = Elem<T>::store(da * silu);
+          out[2][b][q][c] = Elem<T>::store(s * av);
         }
       }
+    }
+    const int rb = row0 + acc.wm * Cfg::WTM + a * 32;
+    auto flush = [&](int o) {
+      T* base = o == 0 ? dH + cw : o == 1 ? dH + n + cw : As + cw;
+      const int ld = o == 2 ? n : n2;
+      stg[o].flush(
+          [&](int r) -> T* { return rb + r < rend ? base + int64_t(rb + r) * ld : nullptr; });
+    };
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {
+#pragma unroll
+      for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) stg[o].put(r32, b * 32 + q * 8 + h * 4, out[o][b][q]);
+      if constexpr (!kAll) flush(o);
+    }
+    if constexpr (kAll) {
+#pragma unroll
+      for (int o = 0; o < 3; ++o) flush(o);
     }
     part += __shfl_xor(part, 32, 64);
     if (acc.lane < 32) red[acc.wn * BM + i] = part;
@@ -135,21 +165,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
   acc.init();
   pipeline<Cfg, true, true>(acc, lds, n2 / Cfg::BK, la, lb, NoTail{});
 
-#pragma unroll
-  for (int a = 0; a < Cfg::MB; ++a) {
-    const int slot = row0 + acc.row(a);
-    if (slot >= rend) continue;
-    T* orow = dXt + int64_t(slot) * d + j0;
-#pragma unroll
-    for (int b = 0; b < Cfg::NB; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        T v[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
-        __builtin_memcpy(orow + acc.col(b, q), v, sizeof(v));
-      }
-  }
+  static_assert(RowStage<T, Cfg::WTN>::BYTES * Cfg::NW <= Cfg::LDS_BYTES, "staging fits");
+  store_acc_staged(acc, lds, [&](int r) -> T* {
+    return row0 + r < rend ? dXt + int64_t(row0 + r) * d + j0 : nullptr;
+  });
 }
 
 // Varlen-K scheduling: expert_order lists experts by descending slot count.
@@ -166,22 +185,14 @@ __device__ __forceinline__ bool varlen_k_tile(int b, int PT, int E, const int32_
   return true;
 }
 
+// Writes a full weight-gradient tile (rows i0.., columns j0..) through the
+// epilogue staging buffers.
 template <class Cfg>
-__device__ __forceinline__ void store_tile(const Accum<Cfg>& acc, typename Cfg::T* out, int ld) {
+__device__ __forceinline__ void store_tile(const Accum<Cfg>& acc, char* lds,
+                                           typename Cfg::T* out, int ld) {
   using T = typename Cfg::T;
-#pragma unroll
-  for (int a = 0; a < Cfg::MB; ++a) {
-    T* orow = out + int64_t(acc.row(a)) * ld;
-#pragma unroll
-    for (int b = 0; b < Cfg::NB; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        T v[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
-        __builtin_memcpy(orow + acc.col(b, q), v, sizeof(v));
-      }
-  }
+  static_assert(RowStage<T, Cfg::WTN>::BYTES * Cfg::NW <= Cfg::LDS_BYTES, "staging fits");
+  store_acc_staged(acc, lds, [&](int r) -> T* { return out + int64_t(r) * ld; });
 }
 
 // Zeroes the rows past the expert's last slot in the final, partial slab of
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
   acc.init();
   VarlenTail<Cfg, BM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
   pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
-  store_tile(acc, dW1 + (int64_t(e) * d + i0) * n2 + j0, n2);
+  store_tile(acc, lds, dW1 + (int64_t(e) * d + i0) * n2 + j0, n2);
 }
 
 // dW2_e[i][j] = sum over the expert's slots k of As[k][i] * dO[tok_k][j].
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
   acc.init();
   VarlenTail<Cfg, BM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
   pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
-  store_tile(acc, dW2 + (int64_t(e) * n + i0) * d + j0, d);
+  store_tile(acc, lds, dW2 + (int64_t(e) * n + i0) * d + j0, d);
 }
 
 template <class Cfg>

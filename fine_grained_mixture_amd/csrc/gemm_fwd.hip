@@ -53,17 +53,20 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
   acc.init();
   pipeline<Cfg, true, false>(acc, lds, d / Cfg::BK, la, lb, NoTail{});
 
+  // Epilogue: H (gate and up halves, rounded to T) and A = SiLU(g) * u from
+  // the rounded values, staged per wave and written as whole rows.
+  using St = RowStage<T, Cfg::WTN / 2>;
+  static_assert(3 * St::BYTES * Cfg::NW <= Cfg::LDS_BYTES, "epilogue staging fits in LDS");
+  char* wbuf = lds + wave_id() * 3 * St::BYTES;
+  const St sg{wbuf}, su{wbuf + St::BYTES}, sa{wbuf + 2 * St::BYTES};
+  const int r32 = acc.lane & 31, h = acc.lane >> 5;
+  const int jw = j0 + Cfg::colblock(acc.wn, 0);  // first gate column of this wave
 #pragma unroll
   for (int a = 0; a < Cfg::MB; ++a) {
-    const int slot = row0 + acc.row(a);
-    if (slot >= rend) continue;
-    T* hrow = H + int64_t(slot) * n2;
-    T* arow = Aact + int64_t(slot) * n;
 #pragma unroll
     for (int b = 0; b < Cfg::NB / 2; ++b) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = j0 + acc.col(b, q);  // gate column in [0, n)
         T hg[4], hu[4], av[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -73,11 +76,18 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
           hu[c] = Elem<T>::store(u);
           av[c] = Elem<T>::store(g * sigmoidf_(g) * u);
         }
-        __builtin_memcpy(hrow + j, hg, sizeof(hg));
-        __builtin_memcpy(hrow + n + j, hu, sizeof(hu));
-        __builtin_memcpy(arow + j, av, sizeof(av));
+        const int col = b * 32 + q * 8 + h * 4;
+        sg.put(r32, col, hg);
+        su.put(r32, col, hu);
+        sa.put(r32, col, av);
       }
     }
+    const int rb = row0 + acc.wm * Cfg::WTM + a * 32;  // first slot of the block
+    sg.flush([&](int r) -> T* { return rb + r < rend ? H + int64_t(rb + r) * n2 + jw : nullptr; });
+    su.flush([&](int r) -> T* {
+      return rb + r < rend ? H + int64_t(rb + r) * n2 + n + jw : nullptr;
+    });
+    sa.flush([&](int r) -> T* { return rb + r < rend ? Aact + int64_t(rb + r) * n + jw : nullptr; });
   }
 }
 
@@ -111,21 +121,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_down(
   acc.init();
   pipeline<Cfg, true, false>(acc, lds, n / Cfg::BK, la, lb, NoTail{});
 
-#pragma unroll
-  for (int a = 0; a < Cfg::MB; ++a) {
-    const int slot = row0 + acc.row(a);
-    if (slot >= rend) continue;
-    T* yrow = Y + int64_t(slot) * d + j0;
-#pragma unroll
-    for (int b = 0; b < Cfg::NB; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        T v[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = Elem<T>::store(acc.acc[a][b][q * 4 + c]);
-        __builtin_memcpy(yrow + acc.col(b, q), v, sizeof(v));
-      }
-  }
+  static_assert(RowStage<T, Cfg::WTN>::BYTES * Cfg::NW <= Cfg::LDS_BYTES, "staging fits");
+  store_acc_staged(acc, lds, [&](int r) -> T* {
+    return row0 + r < rend ? Y + int64_t(row0 + r) * d + j0 : nullptr;
+  });
 }
 
 inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
