@@ -29,30 +29,11 @@ sys.path.insert(0, ROOT)
 
 from fine_grained_mixture_amd import moe  # noqa: E402
 from fine_grained_mixture_amd.inputs import SHAPES, make_layer_inputs  # noqa: E402
+from fine_grained_mixture_amd.profiling import kernel_model, read_traffic  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3    # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-
-
-def kernel_model(name, sh, S, esz=2):
-    """Algorithmic FLOPs and HBM bytes of one launch of each kernel: the
-    operands the method must move once (gathered rows counted once per slot,
-    weights once, transients written and read once), no padded work."""
-    T, d, n, E = sh.T, sh.d, sh.n, sh.E
-    idx = 4 * S  # one int32 per slot
-    m = {
-        "up_swiglu": (4 * S * d * n, esz * (S * d + E * d * 2 * n + S * 2 * n + S * n) + idx),
-        "down": (2 * S * n * d, esz * (S * n + E * n * d + S * d)),
-        "aggregate_O": (2 * S * d, esz * (S * d + T * d) + 2 * idx + 4 * T),
-        "dh": (2 * S * d * n, esz * (S * d + E * n * d + S * 2 * n + S * 2 * n + S * n)
-               + 4 * S + 2 * idx),
-        "dxt": (4 * S * n * d, esz * (S * 2 * n + E * d * 2 * n + S * d)),
-        "aggregate_dX": (S * d, esz * (S * d + T * d) + idx + 4 * T),
-        "dw1": (4 * S * d * n, esz * (S * d + S * 2 * n + E * d * 2 * n) + idx),
-        "dw2": (2 * S * n * d, esz * (S * n + S * d + E * n * d) + idx),
-    }
-    return m.get(name)
 
 
 def restrict_routing(rt, keep):
@@ -212,7 +193,11 @@ def main():
         roof = {"bound": "hbm", "achieved": b_k / dur / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary of
+    # this workload, when it was taken on the current kernel sources
+    roof["traffic"] = read_traffic(
+        os.path.join(ROOT, "profiles", f"hbm_traffic_{sh.name}_{args.mode}.md"), dname)
+    roof["algorithmic_bytes"] = b_k
     roof["kernel"] = dname
     roof["avg_us"] = per[dom] * 1e3
 

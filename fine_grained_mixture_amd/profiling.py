@@ -1,0 +1,211 @@
+"""Kernel cost model and rocprofv3 summaries for the MoE layer.
+
+* ``kernel_model``: algorithmic FLOPs and HBM bytes of one launch of each
+  kernel, from the layer shape and the slot count.  These are what the method
+  has to move: gathered rows once per slot, weights once, each transient
+  written once and read once, outputs once, and no padded work.
+* ``kernel_sources_sha256``: a digest of the HIP sources and the C header,
+  which stamps every counter summary, so that a stale summary (taken on
+  kernels that have changed since) is never reported as current.
+* Command line: turns the CSV files of rocprofv3 runs into the short text
+  summaries kept under ``profiles/``:
+
+    python -m fine_grained_mixture_amd.profiling stats <kernel_stats.csv> <cmd>
+    python -m fine_grained_mixture_amd.profiling traffic --fetch F.csv --write W.csv \
+        --cal-fetch CF.csv --cal-write CW.csv --config 7b --slots S <cmd>
+
+  ``traffic`` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch)
+  by what the same counters read for a plain 1 GiB device-to-device copy of
+  known traffic (1 GiB read and 1 GiB written per launch).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+# rocprofv3 kernel name -> the name the benchmark and the trace events use
+KERNEL_LABELS = {
+    "k_up_swiglu": "up_swiglu", "k_down": "down", "k_dh": "dh", "k_dxt": "dxt",
+    "k_dw1": "dw1", "k_dw2": "dw2",
+}
+# the aggregation kernel runs twice per step: forward (O), then backward (dX)
+AGGREGATE_LABELS = ("aggregate_O", "aggregate_dX")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+
+def kernel_model(name, sh, S, esz=2):
+    """(FLOPs, bytes) of one launch of kernel `name` for layer shape `sh`
+    with S slots (bf16 when esz = 2), or None for kernels without a model."""
+    T, d, n, E = sh.T, sh.d, sh.n, sh.E
+    idx = 4 * S  # one int32 per slot
+    m = {
+        "up_swiglu": (4 * S * d * n, esz * (S * d + E * d * 2 * n + S * 2 * n + S * n) + idx),
+        "down": (2 * S * n * d, esz * (S * n + E * n * d + S * d)),
+        "aggregate_O": (2 * S * d, esz * (S * d + T * d) + 2 * idx + 4 * T),
+        "dh": (2 * S * d * n, esz * (S * d + E * n * d + S * 2 * n + S * 2 * n + S * n)
+               + 4 * S + 2 * idx),
+        "dxt": (4 * S * n * d, esz * (S * 2 * n + E * d * 2 * n + S * d)),
+        "aggregate_dX": (S * d, esz * (S * d + T * d) + idx + 4 * T),
+        "dw1": (4 * S * d * n, esz * (S * d + S * 2 * n + E * d * 2 * n) + idx),
+        "dw2": (2 * S * n * d, esz * (S * n + S * d + E * n * d) + idx),
+    }
+    return m.get(name)
+
+
+def kernel_sources_sha256(root=ROOT):
+    """sha256 over the kernel sources (csrc/*.hip, *.hpp) and include/*.h."""
+    files = sorted(glob.glob(os.path.join(root, "fine_grained_mixture_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(root, "fine_grained_mixture_amd", "csrc", "*.hpp")) +
+                   glob.glob(os.path.join(root, "include", "*.h")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, root).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _base_name(kernel_name):
+    m = re.search(r"(k_\w+|route_\w+|__amd_rocclr_\w+)", kernel_name)
+    return m.group(1) if m else kernel_name
+
+
+def counter_per_dispatch(path, counter):
+    """{label: [value per dispatch, in dispatch order]} of one counter."""
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), _base_name(r["Kernel_Name"]),
+                             float(r["Counter_Value"])))
+    rows.sort()
+    out = collections.defaultdict(list)
+    n_agg = 0
+    for _, k, v in rows:
+        if k == "k_aggregate":
+            k = AGGREGATE_LABELS[n_agg % 2]
+            n_agg += 1
+        else:
+            k = KERNEL_LABELS.get(k, k)
+        out[k].append(v)
+    return out
+
+
+def _mean(v):
+    return sum(v) / len(v)
+
+
+def traffic_table(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """Per kernel: (launches, HBM bytes read, HBM bytes written) per launch,
+    calibrated; plus the two scale factors (counter bytes / true bytes)."""
+    cf = counter_per_dispatch(cal_fetch_csv, "FETCH_SIZE")[COPY_KERNEL]
+    cw = counter_per_dispatch(cal_write_csv, "WRITE_SIZE")[COPY_KERNEL]
+    f_scale = _mean(cf) * 1024 / COPY_BYTES
+    w_scale = _mean(cw) * 1024 / COPY_BYTES
+    fe = counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    wr = counter_per_dispatch(write_csv, "WRITE_SIZE")
+    rows = {}
+    for k in fe:
+        if k not in wr or k == COPY_KERNEL:
+            continue
+        rows[k] = (len(fe[k]), _mean(fe[k]) * 1024 / f_scale, _mean(wr[k]) * 1024 / w_scale)
+    return rows, f_scale, w_scale
+
+
+def read_traffic(path, kernel):
+    """HBM bytes per launch of `kernel` from a committed traffic summary, or
+    None when the summary is missing or was taken on other kernel sources."""
+    try:
+        with open(path) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    m = re.search(r"kernel-sources-sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel_sources_sha256():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 5 and cells[0] == kernel:
+            try:
+                return int(round(float(cells[4]) * 1e6))
+            except ValueError:
+                return None
+    return None
+
+
+def _stats_md(path, cmd):
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["Percentage"])))
+    out = ["Command (run from /tmp with TMPDIR=/tmp; $R is the repository root):", "",
+           "```", cmd, "```", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, pct in rows:
+        out.append(f"| {name} | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _traffic_md(args):
+    sys.path.insert(0, ROOT)
+    from fine_grained_mixture_amd.inputs import SHAPES
+
+    sh = SHAPES[args.config]
+    rows, fs, ws = traffic_table(args.fetch, args.write, args.cal_fetch, args.cal_write)
+    out = ["Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root):", "",
+           "```", *args.cmd, "```", "",
+           f"Calibration: a 1 GiB device-to-device copy ({COPY_KERNEL}) reads "
+           f"FETCH_SIZE = {fs:.3f} x and WRITE_SIZE = {ws:.3f} x its true bytes; the "
+           "figures below are divided by those factors.", "",
+           f"kernel-sources-sha256: {kernel_sources_sha256()}", "",
+           f"Slots S = {args.slots}.  MB = 1e6 bytes per launch.", "",
+           "| kernel | launches | read MB | write MB | HBM MB | algorithmic MB | HBM / algorithmic |",
+           "|---|---|---|---|---|---|---|"]
+    order = ["up_swiglu", "down", "aggregate_O", "dh", "dxt", "aggregate_dX", "dw1", "dw2"]
+    names = order + sorted(k for k in rows if k not in order)
+    for k in names:
+        if k not in rows:
+            continue
+        n, rd, wr = rows[k]
+        model = kernel_model(k, sh, args.slots)
+        alg = f"{model[1] / 1e6:.1f}" if model else "-"
+        ratio = f"{(rd + wr) / model[1]:.2f}" if model else "-"
+        out.append(f"| {k} | {n} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | "
+                   f"{alg} | {ratio} |")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats", help="kernel-trace statistics table")
+    s.add_argument("csv")
+    s.add_argument("cmd")
+    t = sub.add_parser("traffic", help="HBM traffic table from FETCH_SIZE / WRITE_SIZE")
+    for a in ("--fetch", "--write", "--cal-fetch", "--cal-write"):
+        t.add_argument(a, required=True)
+    t.add_argument("--config", default="7b")
+    t.add_argument("--slots", type=int, required=True)
+    t.add_argument("cmd", nargs="+", help="the commands that produced the CSV files")
+    args = ap.parse_args(argv)
+    if args.what == "stats":
+        sys.stdout.write(_stats_md(args.csv, args.cmd))
+    else:
+        sys.stdout.write(_traffic_md(args))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,31 @@
+"""Host-side checks of the benchmark's cost model and counter summaries."""
+from fine_grained_mixture_amd import profiling
+from fine_grained_mixture_amd.inputs import SHAPES
+
+
+def _summary(tmp_path, digest):
+    p = tmp_path / "t.md"
+    p.write_text(f"kernel-sources-sha256: {digest}\n\n"
+                 "| kernel | launches | read MB | write MB | HBM MB | algorithmic MB | r |\n"
+                 "|---|---|---|---|---|---|---|\n"
+                 "| dxt | 3 | 400.0 | 400.0 | 800.5 | 738.2 | 1.08 |\n")
+    return p
+
+
+def test_traffic_only_for_current_sources(tmp_path):
+    cur = profiling.kernel_sources_sha256()
+    assert profiling.read_traffic(str(_summary(tmp_path, cur)), "dxt") == 800_500_000
+    assert profiling.read_traffic(str(_summary(tmp_path, cur)), "dw1") is None
+    stale = ("0" if cur[0] != "0" else "1") + cur[1:]
+    assert profiling.read_traffic(str(_summary(tmp_path, stale)), "dxt") is None
+    assert profiling.read_traffic(str(tmp_path / "missing.md"), "dxt") is None
+
+
+def test_kernel_model_flops_sum_to_layer_flops():
+    # the six GEMMs carry 18 S n d FLOPs; the aggregations add 3 S d
+    sh = SHAPES["7b"]
+    S = sh.T * sh.K
+    gemm = sum(profiling.kernel_model(k, sh, S)[0]
+               for k in ("up_swiglu", "down", "dh", "dxt", "dw1", "dw2"))
+    assert gemm == 18 * S * sh.n * sh.d == sh.flops
+    assert profiling.kernel_model("route_topk", sh, S) is None
