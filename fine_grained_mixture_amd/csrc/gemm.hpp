@@ -88,8 +88,21 @@ struct TileCfg {
 // ---------------------------------------------------------------------------
 // Low-level helpers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void dma16(const void* g, char* lds_wave) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave, 16, 0, 0);
+// Buffer descriptor of `bytes` bytes at the wave-uniform address `base`
+// (raw, unswizzled; word 3 is the gfx9-family default).  A load whose offset
+// lies at or past `bytes` returns zeros instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from `rs` at byte offset `voff` straight into LDS: lane
+// L of the wave writes lds_wave + 16 L.  The MUBUF form is used rather than
+// the global (FLAT-encoded) one: the compiler's wait-counter pass treats a
+// FLAT DMA as a possible out-of-order LDS access and would then wait for
+// every outstanding fragment read (lgkmcnt(0)) before each MFMA.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, char* lds_wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_wave, 16, voff, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained.
@@ -131,68 +144,78 @@ __device__ __forceinline__ int mswz(int k) {
 // ---------------------------------------------------------------------------
 
 // K-major operand whose ROWS source rows are fixed over the k loop: row r's
-// k-values for slab s start at rowptr(r) + KB s bytes.
+// k-values for slab s start at byte rowoff(r) + KB s of a buffer of `bytes`
+// bytes at `base`.
 template <class Cfg, int ROWS>
 struct KLoad {
   static constexpr int KB = Cfg::KB, CPR = KB / 16;  // 16-byte chunks per row
   static_assert((ROWS * KB) % (Cfg::kThreads * 16) == 0, "rows");
   static constexpr int NI = ROWS * KB / (Cfg::kThreads * 16);
-  const char* p[NI];
+  rsrc_t rs;
+  uint32_t off[NI];
   int w;
 
-  template <class RowPtr>
-  __device__ __forceinline__ void init(RowPtr rowptr) {
+  template <class RowOff>
+  __device__ __forceinline__ void init(const void* base, uint32_t bytes, RowOff rowoff) {
+    rs = make_rsrc(base, bytes);
     w = wave_id();
     const int L = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int idx = (i * Cfg::NW + w) * 64 + L;
       const int r = idx / CPR, pos = idx % CPR;
-      p[i] = reinterpret_cast<const char*>(rowptr(r)) + ((pos ^ kswz<KB>(r)) << 4);
+      off[i] = uint32_t(rowoff(r)) + uint32_t((pos ^ kswz<KB>(r)) << 4);
     }
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(p[i] + s * KB, tile + (i * Cfg::NW + w) * 1024);
+    for (int i = 0; i < NI; ++i)
+      dma16(rs, off[i] + uint32_t(s * KB), tile + (i * Cfg::NW + w) * 1024);
   }
 };
 
 // MN-major operand with a fixed row stride (weights): row k of slab s is at
-// base + (s*BK + k) * ld_bytes; col_bytes(c) is the byte offset of logical
-// 16-byte chunk c of the tile row inside a source row.
+// byte (s*BK + k) * ld_bytes of a buffer of `bytes` bytes at `base`;
+// col_bytes(c) is the byte offset of logical 16-byte chunk c of the tile row
+// inside a source row.
 template <class Cfg, int COLS>
 struct MNLoad {
   using T = typename Cfg::T;
   static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
   static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
   static_assert(NI >= 1 && (Cfg::BK * RB) % (Cfg::kThreads * 16) == 0, "tile size");
-  const char* p[NI];
-  int64_t step;
+  rsrc_t rs;
+  uint32_t off[NI];
+  uint32_t step;
   int w;
 
   template <class ColBytes>
-  __device__ __forceinline__ void init(const void* base, int64_t ld_bytes, ColBytes col_bytes) {
+  __device__ __forceinline__ void init(const void* base, uint32_t bytes, uint32_t ld_bytes,
+                                       ColBytes col_bytes) {
+    rs = make_rsrc(base, bytes);
     w = wave_id();
     const int L = threadIdx.x & 63;
-    step = int64_t(Cfg::BK) * ld_bytes;
+    step = uint32_t(Cfg::BK) * ld_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int idx = (i * Cfg::NW + w) * 64 + L;
       const int k = idx / CH, pos = idx % CH;
-      p[i] = reinterpret_cast<const char*>(base) + k * ld_bytes + col_bytes(pos ^ mswz<CH>(k));
+      off[i] = uint32_t(k) * ld_bytes + uint32_t(col_bytes(pos ^ mswz<CH>(k)));
     }
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(p[i] + s * step, tile + (i * Cfg::NW + w) * 1024);
+    for (int i = 0; i < NI; ++i)
+      dma16(rs, off[i] + uint32_t(s) * step, tile + (i * Cfg::NW + w) * 1024);
   }
 };
 
 // MN-major operand whose rows are an expert's slots (varlen-K): row k of
 // slab s is slot kb + s*BK + k, read from source row idx[slot] (GATHER) or
-// row slot; slots past the expert's end read its last slot and are zeroed in
-// LDS afterwards.  The gather indices are wave-uniform per row and are read
-// with scalar loads, so they do not count against the DMA wait counter.
+// row slot of a buffer of `bytes` bytes at `base`; slots past the expert's
+// end read its last slot and are zeroed in LDS afterwards.  The gather
+// indices are wave-uniform per row and are read with scalar loads, so they
+// do not count against the DMA wait counter.
 template <class Cfg, int COLS, bool GATHER>
 struct SlotLoad {
   using T = typename Cfg::T;
@@ -200,16 +223,17 @@ struct SlotLoad {
   static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
   static constexpr int RPI = 64 / CH;  // tile rows per DMA instruction
   static_assert(NI >= 1 && RPI >= 1 && (!GATHER || RPI <= 4), "tile size");
-  const char* base;
+  rsrc_t rs;
   const int32_t* idx;
-  int64_t ld_bytes;
-  int colb[NI];
+  uint32_t ld_bytes;
+  uint32_t colb[NI];
   int kb, klast, w, sub;
 
   template <class ColBytes>
-  __device__ __forceinline__ void init(const void* b, int64_t ldb, ColBytes col_bytes,
-                                       const int32_t* index, int kbeg, int kend) {
-    base = reinterpret_cast<const char*>(b);
+  __device__ __forceinline__ void init(const void* base, uint32_t bytes, uint32_t ldb,
+                                       ColBytes col_bytes, const int32_t* index, int kbeg,
+                                       int kend) {
+    rs = make_rsrc(base, bytes);
     idx = index;
     ld_bytes = ldb;
     kb = kbeg;
@@ -221,7 +245,7 @@ struct SlotLoad {
     for (int i = 0; i < NI; ++i) {
       const int q = (i * Cfg::NW + w) * 64 + L;
       const int k = q / CH, pos = q % CH;
-      colb[i] = col_bytes(pos ^ mswz<CH>(k));
+      colb[i] = uint32_t(col_bytes(pos ^ mswz<CH>(k)));
     }
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
@@ -239,7 +263,7 @@ struct SlotLoad {
       } else {
         row = min(k0 + sub, klast);
       }
-      dma16(base + row * ld_bytes + colb[i], tile + (i * Cfg::NW + w) * 1024);
+      dma16(rs, uint32_t(row) * ld_bytes + colb[i], tile + (i * Cfg::NW + w) * 1024);
     }
   }
 };
@@ -354,11 +378,16 @@ struct Accum {
       if (kc + 1 < Cfg::KCH) frags<AK, BKM>(fa[(kc + 1) & 1], fb[(kc + 1) & 1], As, Bs, kc + 1);
       // keep those reads ahead of this chunk's MFMAs
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int a = 0; a < Cfg::MB; ++a)
-#pragma unroll
-        for (int b = 0; b < Cfg::NB; ++b) mma16(acc[a][b], fb[kc & 1][b], fa[kc & 1][a]);
+      mma(fa[kc & 1], fb[kc & 1]);
     }
+  }
+
+  // The MFMAs of one k chunk.
+  __device__ __forceinline__ void mma(const Oct<T> (&fa)[Cfg::MB], const Oct<T> (&fb)[Cfg::NB]) {
+#pragma unroll
+    for (int a = 0; a < Cfg::MB; ++a)
+#pragma unroll
+      for (int b = 0; b < Cfg::NB; ++b) mma16(acc[a][b], fb[b], fa[a]);
   }
 
   // Tile row of block a for this lane; tile column of the 4-column group q.
@@ -388,9 +417,11 @@ __device__ __forceinline__ void pipeline_step(Accum<Cfg>& acc, const char* __res
 // Multi-stage DMA pipeline over `nslabs` slabs.  Slab s lives in stage s % S;
 // at the top of iteration s the wave waits until its own DMA for slab s has
 // landed (later slabs may stay in flight), the barrier makes every wave's
-// part visible, and the DMA for slab s + S - 1 is issued into the stage that
-// was consumed in iteration s - 1.  `tail(s, stage)` may patch the stage
-// (it must end with its own wait + barrier if it writes LDS).
+// part visible and shows that every wave is done with slab s - 1, and the
+// DMA for slab s + S - 1 is issued into that stage, so each slab has S - 1
+// slabs of compute to arrive in.  `tail(s, stage)` may patch the stage (it
+// must end with its own wait + barrier if it writes LDS).  Ends with a
+// barrier, so the caller may reuse the LDS.
 template <class Cfg, bool AK, bool BKM, class LA, class LB, class Tail>
 __device__ __forceinline__ void pipeline(Accum<Cfg>& acc, char* lds, int nslabs, const LA& la,
                                          const LB& lb, Tail&& tail) {

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
     T* __restrict__ dH, T* __restrict__ As, float* __restrict__ dS,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
-    const float* __restrict__ slot_weight, const int32_t* __restrict__ totals, int d) {
+    const float* __restrict__ slot_weight, const int32_t* __restrict__ totals, int d, int ntok) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WGN = Cfg::WGN;
   constexpr int n = BN, n2 = 2 * BN, SUB = kTileM / BM;
@@ -41,14 +41,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
   if (row0 >= rend) return;
   const int tok0 = slot_token[row0];
 
+  const uint32_t orow = uint32_t(d) * sizeof(T);
   KLoad<Cfg, BM> la;
-  la.init([&](int r) {
+  la.init(dO, uint32_t(ntok) * orow, [&](int r) {
     const int slot = row0 + r;
-    return dO + int64_t(slot < rend ? slot_token[slot] : tok0) * d;
+    return uint32_t(slot < rend ? slot_token[slot] : tok0) * orow;
   });
-  const T* w2 = W2 + int64_t(e) * n * d;
   KLoad<Cfg, BN> lb;
-  lb.init([&](int j) { return w2 + int64_t(j) * d; });
+  lb.init(W2 + int64_t(e) * n * d, uint32_t(n) * orow, [&](int j) { return uint32_t(j) * orow; });
 
   Accum<Cfg> acc;
   acc.init();
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
     const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
-    int n) {
+    int n, int nslot) {
   static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BN = Cfg::BN;
@@ -152,14 +152,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
   const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
   const int j0 = nt * BN;
 
+  const uint32_t hrow = uint32_t(n2) * sizeof(T);
   KLoad<Cfg, kTileM> la;
-  la.init([&](int r) {
+  la.init(dH, uint32_t(nslot) * hrow, [&](int r) {
     const int slot = row0 + r;
-    return dH + int64_t(slot < rend ? slot : row0) * n2;
+    return uint32_t(slot < rend ? slot : row0) * hrow;
   });
-  const T* w1 = W1 + int64_t(e) * d * n2;
   KLoad<Cfg, BN> lb;
-  lb.init([&](int c) { return w1 + int64_t(j0 + c) * n2; });
+  lb.init(W1 + int64_t(e) * d * n2, uint32_t(d) * hrow,
+          [&](int c) { return uint32_t(j0 + c) * hrow; });
 
   Accum<Cfg> acc;
   acc.init();
@@ -215,7 +216,7 @@ template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
     const T* __restrict__ X, const T* __restrict__ dH, T* __restrict__ dW1,
     const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
-    const int32_t* __restrict__ slot_token, int E, int d, int n) {
+    const int32_t* __restrict__ slot_token, int E, int d, int n, int ntok, int nslot) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BM = Cfg::BM, BN = Cfg::BN, EPC = 16 / int(sizeof(T));
   const int n2 = 2 * n, TN = n2 / BN, PT = (d / BM) * TN;
@@ -226,11 +227,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
   SlotLoad<Cfg, BM, true> la;
-  la.init(X, int64_t(d) * sizeof(T), [=](int c) { return int((i0 + c * EPC) * sizeof(T)); },
-          slot_token, kb, ke);
+  la.init(X, uint32_t(ntok) * d * sizeof(T), uint32_t(d) * sizeof(T),
+          [=](int c) { return int((i0 + c * EPC) * sizeof(T)); }, slot_token, kb, ke);
   SlotLoad<Cfg, BN, false> lb;
-  lb.init(dH, int64_t(n2) * sizeof(T), [=](int c) { return int((j0 + c * EPC) * sizeof(T)); },
-          nullptr, kb, ke);
+  lb.init(dH, uint32_t(nslot) * n2 * sizeof(T), uint32_t(n2) * sizeof(T),
+          [=](int c) { return int((j0 + c * EPC) * sizeof(T)); }, nullptr, kb, ke);
 
   Accum<Cfg> acc;
   acc.init();
@@ -244,7 +245,7 @@ template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
     const T* __restrict__ As, const T* __restrict__ dO, T* __restrict__ dW2,
     const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
-    const int32_t* __restrict__ slot_token, int E, int d, int n) {
+    const int32_t* __restrict__ slot_token, int E, int d, int n, int ntok, int nslot) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BM = Cfg::BM, BN = Cfg::BN, EPC = 16 / int(sizeof(T));
   const int TN = d / BN, PT = (n / BM) * TN;
@@ -255,11 +256,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
   SlotLoad<Cfg, BM, false> la;
-  la.init(As, int64_t(n) * sizeof(T), [=](int c) { return int((i0 + c * EPC) * sizeof(T)); },
-          nullptr, kb, ke);
+  la.init(As, uint32_t(nslot) * n * sizeof(T), uint32_t(n) * sizeof(T),
+          [=](int c) { return int((i0 + c * EPC) * sizeof(T)); }, nullptr, kb, ke);
   SlotLoad<Cfg, BN, true> lb;
-  lb.init(dO, int64_t(d) * sizeof(T), [=](int c) { return int((j0 + c * EPC) * sizeof(T)); },
-          slot_token, kb, ke);
+  lb.init(dO, uint32_t(ntok) * d * sizeof(T), uint32_t(d) * sizeof(T),
+          [=](int c) { return int((j0 + c * EPC) * sizeof(T)); }, slot_token, kb, ke);
 
   Accum<Cfg> acc;
   acc.init();
@@ -276,7 +277,7 @@ void dh_launch(const LayerArgs& a, const void* dO, const void* W2, const void* H
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dO),
                      static_cast<const T*>(W2), static_cast<const T*>(H), static_cast<T*>(dH),
                      static_cast<T*>(As), dS, a.tile_expert, a.tile_row, a.expert_offsets,
-                     a.slot_token, a.slot_weight, a.totals, a.d);
+                     a.slot_token, a.slot_weight, a.totals, a.d, a.T);
 }
 
 template <class T>
@@ -301,7 +302,7 @@ void dxt_launch(const LayerArgs& a, const void* dH, const void* W1, void* dXt, h
   hipLaunchKernelGGL((k_dxt<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dH),
                      static_cast<const T*>(W1), static_cast<T*>(dXt), a.tile_expert, a.tile_row,
-                     a.expert_offsets, a.totals, a.d, a.n);
+                     a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
 }
 
 inline unsigned varlen_k_grid(int E, int PT) { return unsigned(8 * ((E + 7) / 8) * PT); }
@@ -313,7 +314,8 @@ void dw1_launch(const LayerArgs& a, const void* X, const void* dH, void* dW1, hi
                      dim3(varlen_k_grid(a.E, (a.d / Cfg::BM) * (2 * a.n / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
                      static_cast<const T*>(dH), static_cast<T*>(dW1), a.expert_order,
-                     a.expert_offsets, a.slot_token, a.E, a.d, a.n);
+                     a.expert_offsets, a.slot_token, a.E, a.d, a.n, a.T,
+                     int(a.slot_cap));
 }
 
 template <class Cfg>
@@ -322,7 +324,8 @@ void dw2_launch(const LayerArgs& a, const void* As, const void* dO, void* dW2, h
   hipLaunchKernelGGL((k_dw2<Cfg>), dim3(varlen_k_grid(a.E, (a.n / Cfg::BM) * (a.d / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(As),
                      static_cast<const T*>(dO), static_cast<T*>(dW2), a.expert_order,
-                     a.expert_offsets, a.slot_token, a.E, a.d, a.n);
+                     a.expert_offsets, a.slot_token, a.E, a.d, a.n, a.T,
+                     int(a.slot_cap));
 }
 
 }  // namespace

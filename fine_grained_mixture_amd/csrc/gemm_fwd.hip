@@ -26,7 +26,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
     const T* __restrict__ X, const T* __restrict__ W1, T* __restrict__ H, T* __restrict__ Aact,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
-    const int32_t* __restrict__ totals, int d, int n) {
+    const int32_t* __restrict__ totals, int d, int n, int ntok) {
   static_assert(Cfg::PAIRED && Cfg::BM == kTileM, "paired 128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BN = Cfg::BN, HALF = BN / 2, EPC = 16 / int(sizeof(T));
@@ -38,13 +38,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
   const int j0 = nt * HALF, n2 = 2 * n;
   const int tok0 = slot_token[row0];
 
+  const uint32_t xrow = uint32_t(d) * sizeof(T);
   KLoad<Cfg, kTileM> la;
-  la.init([&](int r) {
+  la.init(X, uint32_t(ntok) * xrow, [&](int r) {
     const int slot = row0 + r;
-    return X + int64_t(slot < rend ? slot_token[slot] : tok0) * d;
+    return uint32_t(slot < rend ? slot_token[slot] : tok0) * xrow;
   });
   MNLoad<Cfg, BN> lb;
-  lb.init(W1 + int64_t(e) * d * n2, int64_t(n2) * sizeof(T), [=](int c) {
+  lb.init(W1 + int64_t(e) * d * n2, uint32_t(d) * n2 * sizeof(T), uint32_t(n2) * sizeof(T),
+          [=](int c) {
     const int ce = c * EPC;
     return int((ce < HALF ? j0 + ce : n + j0 + ce - HALF) * sizeof(T));
   });
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_down(
     const T* __restrict__ Aact, const T* __restrict__ W2, T* __restrict__ Y,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
-    int n) {
+    int n, int nslot) {
   static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BN = Cfg::BN, EPC = 16 / int(sizeof(T));
@@ -108,13 +110,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_down(
   const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
   const int j0 = nt * BN;
 
+  const uint32_t arow = uint32_t(n) * sizeof(T);
   KLoad<Cfg, kTileM> la;
-  la.init([&](int r) {
+  la.init(Aact, uint32_t(nslot) * arow, [&](int r) {
     const int slot = row0 + r;
-    return Aact + int64_t(slot < rend ? slot : row0) * n;
+    return uint32_t(slot < rend ? slot : row0) * arow;
   });
   MNLoad<Cfg, BN> lb;
-  lb.init(W2 + int64_t(e) * n * d, int64_t(d) * sizeof(T),
+  lb.init(W2 + int64_t(e) * n * d, uint32_t(n) * d * sizeof(T), uint32_t(d) * sizeof(T),
           [=](int c) { return int((j0 + c * EPC) * sizeof(T)); });
 
   Accum<Cfg> acc;
@@ -138,7 +141,7 @@ void up_launch(const LayerArgs& a, const void* X, const void* W1, void* H, void*
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
                      static_cast<const T*>(W1), static_cast<T*>(H), static_cast<T*>(Aact),
                      a.tile_expert, a.tile_row, a.expert_offsets, a.slot_token, a.totals, a.d,
-                     a.n);
+                     a.n, a.T);
 }
 
 template <class Cfg>
@@ -147,7 +150,7 @@ void down_launch(const LayerArgs& a, const void* Aact, const void* W2, void* Y, 
   hipLaunchKernelGGL((k_down<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(Aact),
                      static_cast<const T*>(W2), static_cast<T*>(Y), a.tile_expert, a.tile_row,
-                     a.expert_offsets, a.totals, a.d, a.n);
+                     a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
 }
 
 }  // namespace

@@ -28,10 +28,15 @@ int check_problem(const moe_problem* p) {
   if (p->K > 32 || p->E > 1024 || p->M_tile > 1024) return MOE_ERR_UNSUPPORTED;
   if (p->d % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (p->n != 64 && p->n != 128 && p->n != 256 && p->n != 384) return MOE_ERR_UNSUPPORTED;
-  // Kernels index rows with 32-bit element offsets.
+  // Kernels index rows with 32-bit element offsets, and the GEMM operand
+  // loads address each array through a buffer descriptor with a 32-bit byte
+  // extent.
   const int64_t slot_cap = p->T * p->K + p->E * p->M_tile;
   if (p->T > INT_MAX / 64 || p->E > INT_MAX / p->T) return MOE_ERR_UNSUPPORTED;
   if (p->T * p->d >= INT_MAX || slot_cap * 2 * p->n >= INT_MAX || slot_cap * p->d >= INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t es = p->dtype == MOE_F32 ? 4 : 2, lim = int64_t(UINT32_MAX);
+  if (p->T * p->d * es > lim || slot_cap * 2 * p->n * es > lim || slot_cap * p->d * es > lim)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

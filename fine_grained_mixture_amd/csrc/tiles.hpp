@@ -19,36 +19,36 @@ namespace moe {
 #endif
 
 #if MOE_TILE_VARIANT == 1
-// four waves, 128 x 256, 64-byte slabs, three stages: 72 KB, two workgroups/CU
-using UpWide = TileCfg<bf16_t, 128, 256, 2, 2, 3, 64, true>;
-using RowsWide = TileCfg<bf16_t, 128, 256, 2, 2, 3, 64>;
-using GradSquare = TileCfg<bf16_t, 128, 256, 2, 2, 3, 64>;
-#elif MOE_TILE_VARIANT == 2
-// eight waves, 128 x 256, 128-byte slabs, three stages (147 KB)
-using UpWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128, true>;
-using RowsWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
-using GradSquare = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
-#elif MOE_TILE_VARIANT == 3
-// four waves, 128 x 256, 64-byte slabs, two stages: 48 KB, three workgroups/CU
-using UpWide = TileCfg<bf16_t, 128, 256, 2, 2, 2, 64, true>;
-using RowsWide = TileCfg<bf16_t, 128, 256, 2, 2, 2, 64>;
-using GradSquare = TileCfg<bf16_t, 128, 256, 2, 2, 2, 64>;
-#elif MOE_TILE_VARIANT == 4
-// four waves, 128 x 128, 128-byte slabs, two stages: 64 KB, two workgroups/CU
-using UpWide = TileCfg<bf16_t, 128, 128, 2, 2, 2, 128, true>;
-using RowsWide = TileCfg<bf16_t, 128, 128, 2, 2, 2, 128>;
-using GradSquare = TileCfg<bf16_t, 128, 128, 2, 2, 2, 128>;
-#else
+// 64-byte slabs: three stages for the 128 x 512 tiles, four for 256 x 256
 using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 3, 64, true>;
 using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 3, 64>;
 using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 4, 64>;
+using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
+#elif MOE_TILE_VARIANT == 2
+// as the default, with four stages of 64-byte slabs for the weight gradients
+using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
+using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
+using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 4, 64>;
+using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
+#elif MOE_TILE_VARIANT == 3
+// as the default, with four stages of 64-byte slabs for dH
+using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
+using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
+using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
+using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 4, 64>;
+#else
+// 128-byte slabs (one full cache line per row), two stages for the wide
+// tiles, three for dH (whose H reloads in the epilogue favour a deeper ring)
+using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
+using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
+using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
+using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 #endif
 
 using UpMid = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128, true>;
 using UpNarrow = TileCfg<bf16_t, 128, 128, 2, 2, 3, 128, true>;
 using RowsMid = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 using RowsNarrow = TileCfg<bf16_t, 128, 128, 2, 2, 3, 128>;
-using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 using GradTall = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 using GradSmall = TileCfg<bf16_t, 128, 128, 2, 2, 3, 128>;
 
