@@ -62,6 +62,20 @@ __device__ __forceinline__ void oct_load(Oct<T>& o, const T* p) {
   }
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) load of an octet that is read once: it does not
+// displace reusable lines from the caches.
+template <class T>
+__device__ __forceinline__ void oct_load_nt(Oct<T>& o, const T* p) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int i = 0; i < Oct<T>::kWords / 4; ++i) {
+    const u32x4_t v = __builtin_nontemporal_load(q + i);
+    o.w[4 * i + 0] = v[0]; o.w[4 * i + 1] = v[1]; o.w[4 * i + 2] = v[2]; o.w[4 * i + 3] = v[3];
+  }
+}
+
 template <class T>
 __device__ __forceinline__ void oct_store(T* p, const Oct<T>& o) {
   uint4* q = reinterpret_cast<uint4*>(p);

@@ -463,7 +463,8 @@ struct NoTail {
 // block (lane l: row l % 32, four consecutive columns per MFMA group) into a
 // wave-private LDS buffer, then writes whole rows to global memory with
 // 16-byte stores, so each store instruction covers several full 128-byte
-// lines instead of 32 partial ones.  Rows are padded by 8 bytes so that the
+// lines instead of 32 partial ones.  The stores are non-temporal: every
+// output here is read at most once, by a later kernel.  Rows are padded by 8 bytes so that the
 // 32 rows written at one column fall in distinct banks.
 template <class T, int COLS>
 struct RowStage {
@@ -489,8 +490,10 @@ struct RowStage {
       const uint2 lo = *reinterpret_cast<const uint2*>(src);
       const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
       T* g = rowptr(r);
-      if (g) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(g) + c * 16) =
-          make_uint4(lo.x, lo.y, hi.x, hi.y);
+      if (g) {
+        const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(g) + c * 16));
+      }
     }
     asm volatile("" ::: "memory");  // read-back before the next deposits
   }
