@@ -11,6 +11,8 @@
 //   k_dxt   dX~_e = dH_e W1_e^T
 //   k_dw1   dW1_e = X[I_e]^T dH_e        (varlen-K)
 //   k_dw2   dW2_e = (s*A)_e^T dO[I_e]    (varlen-K)
+#include <algorithm>
+
 #include "gemm.hpp"
 #include "internal.hpp"
 #include "tiles.hpp"
@@ -172,18 +174,158 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
   });
 }
 
-// Varlen-K scheduling: expert_order lists experts by descending slot count.
-// Ranks q are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8),
-// and all PT output tiles of one expert stay on one XCD, so its gathered rows
-// are fetched into one L2; the largest experts start first.
-__device__ __forceinline__ bool varlen_k_tile(int b, int PT, int E, const int32_t* order,
-                                              int* e, int* tile) {
+// Varlen-K scheduling.  The contraction of an expert with more than KC rows
+// is cut into chunks of KC rows, so that no single tile can hold up the end
+// of the kernel; every other expert is one chunk.  A plan lists the chunks
+// ("items") by expert rank (descending slot count, so the largest work starts
+// first); item i carries its expert, its row range and, when the expert is
+// split, the index of its fp32 partial-sum slab.  The PT output tiles of one
+// item stay on one XCD (block b runs on XCD b % 8) so that the item's
+// gathered rows are fetched into one L2.
+struct VarlenItem {
+  int e, kb, ke, pslot;  // pslot < 0: the item covers the whole expert
+};
+struct VarlenSplit {
+  int e, pbase, nch, pad;  // expert, first partial slab, number of chunks
+};
+
+__device__ __forceinline__ bool varlen_item(int b, int PT, const int* n_items,
+                                            const VarlenItem* items, VarlenItem* it,
+                                            int* tile) {
   const int xcd = b % 8, local = b / 8;
-  const int q = (local / PT) * 8 + xcd;
-  if (q >= E) return false;
-  *e = order[q];
+  const int i = (local / PT) * 8 + xcd;
+  if (i >= *n_items) return false;
+  *it = items[i];
   *tile = local % PT;
   return true;
+}
+
+// One workgroup: the plans of both weight-gradient kernels (chunk sizes kc1,
+// kc2).  Thread q handles expert rank q (E <= 1024).
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(x, o, 64);
+    if (lane >= o) x += u;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      const int t = sh[w];
+      sh[w] = run;
+      run += t;
+    }
+    sh[kPlanThreads / 64] = run;
+  }
+  __syncthreads();
+  const int r = sh[wv] + x - v;
+  *total = sh[kPlanThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ void plan_one(const int32_t* offsets, const int32_t* order, int E,
+                                         int kc, int* header, VarlenItem* items,
+                                         VarlenSplit* splits, int* sh) {
+  const int q = threadIdx.x;
+  int e = 0, beg = 0, cnt = 0, nch = 0;
+  if (q < E) {
+    e = order[q];
+    beg = offsets[e];
+    cnt = offsets[e + 1] - beg;
+    nch = cnt > kc ? (cnt + kc - 1) / kc : 1;
+  }
+  const bool split = nch > 1;
+  int n_items, n_part, n_split;
+  const int ib = block_excl_scan(nch, sh, &n_items);
+  const int pb = block_excl_scan(split ? nch : 0, sh, &n_part);
+  const int sj = block_excl_scan(split ? 1 : 0, sh, &n_split);
+  for (int c = 0; c < nch; ++c) {
+    const int kb = beg + c * kc;
+    items[ib + c] = VarlenItem{e, kb, min(kb + kc, beg + cnt), split ? pb + c : -1};
+  }
+  if (split) splits[sj] = VarlenSplit{e, pb, nch, 0};
+  if (q == 0) {
+    header[0] = n_items;
+    header[1] = n_split;
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ order, int E, int kc1,
+    int kc2, int* header1, VarlenItem* items1, VarlenSplit* splits1, int* header2,
+    VarlenItem* items2, VarlenSplit* splits2) {
+  __shared__ int sh[kPlanThreads / 64 + 1];
+  plan_one(offsets, order, E, kc1, header1, items1, splits1, sh);
+  plan_one(offsets, order, E, kc2, header2, items2, splits2, sh);
+}
+
+// out_e = sum over the chunks of a split expert of its fp32 partials, in
+// chunk order (so the result does not depend on which chunk finished first).
+// Work unit u = j * gy + g covers split expert j, elements g*2048 .. +2048
+// (eight per thread); the blocks stride over the units that exist, and the
+// chunk loads are issued four at a time so that they are in flight together.
+template <class T>
+__global__ __launch_bounds__(256) void k_varlen_reduce(const int* __restrict__ header,
+                                                       const VarlenSplit* __restrict__ splits,
+                                                       const float* __restrict__ partials,
+                                                       T* __restrict__ out, int64_t mn, int gy) {
+  const int units = header[1] * gy;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const VarlenSplit sp = splits[u / gy];
+    const int64_t i = (int64_t(u % gy) * 256 + threadIdx.x) * 8;
+    if (i >= mn) continue;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+    for (int k0 = 0; k0 < sp.nch; k0 += 4) {
+      float4 x[4], y[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (k0 + v < sp.nch) {
+          const float4* q =
+              reinterpret_cast<const float4*>(partials + (sp.pbase + k0 + v) * mn + i);
+          x[v] = q[0];
+          y[v] = q[1];
+        } else {
+          x[v] = y[v] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {  // chunk order
+        acc[0] += x[v].x; acc[1] += x[v].y; acc[2] += x[v].z; acc[3] += x[v].w;
+        acc[4] += y[v].x; acc[5] += y[v].y; acc[6] += y[v].z; acc[7] += y[v].w;
+      }
+    }
+    Oct<T> r;
+    oct_from(r, acc);
+    oct_store(out + sp.e * mn + i, r);
+  }
+}
+
+// fp32 partial of one output tile: lane l holds four consecutive columns of
+// row l % 32 of each 32 x 32 block, written as one 16-byte store.
+template <class Cfg>
+__device__ __forceinline__ void store_tile_f32(const Accum<Cfg>& acc, float* out, int ld) {
+#pragma unroll
+  for (int a = 0; a < Cfg::MB; ++a)
+#pragma unroll
+    for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t v = {__float_as_uint(acc.acc[a][b][q * 4 + 0]),
+                           __float_as_uint(acc.acc[a][b][q * 4 + 1]),
+                           __float_as_uint(acc.acc[a][b][q * 4 + 2]),
+                           __float_as_uint(acc.acc[a][b][q * 4 + 3])};
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4_t*>(out + int64_t(acc.row(a)) * ld + acc.col(b, q)));
+      }
 }
 
 // Writes a full weight-gradient tile (rows i0.., columns j0..) through the
@@ -215,15 +357,17 @@ struct VarlenTail {
 template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
     const T* __restrict__ X, const T* __restrict__ dH, T* __restrict__ dW1,
-    const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
-    const int32_t* __restrict__ slot_token, int E, int d, int n, int ntok, int nslot) {
+    float* __restrict__ partials, const int* __restrict__ n_items,
+    const VarlenItem* __restrict__ items, const int32_t* __restrict__ slot_token, int d, int n,
+    int ntok, int nslot) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BM = Cfg::BM, BN = Cfg::BN, EPC = 16 / int(sizeof(T));
   const int n2 = 2 * n, TN = n2 / BN, PT = (d / BM) * TN;
-  int e, tile;
-  if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
+  VarlenItem it;
+  int tile;
+  if (!varlen_item(blockIdx.x, PT, n_items, items, &it, &tile)) return;
   const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
-  const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
+  const int kb = it.kb, ke = it.ke;
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
   SlotLoad<Cfg, BM, true> la;
@@ -237,22 +381,27 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
   acc.init();
   VarlenTail<Cfg, BM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
   pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
-  store_tile(acc, lds, dW1 + (int64_t(e) * d + i0) * n2 + j0, n2);
+  if (it.pslot < 0)
+    store_tile(acc, lds, dW1 + (int64_t(it.e) * d + i0) * n2 + j0, n2);
+  else
+    store_tile_f32(acc, partials + (int64_t(it.pslot) * d + i0) * n2 + j0, n2);
 }
 
 // dW2_e[i][j] = sum over the expert's slots k of As[k][i] * dO[tok_k][j].
 template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
     const T* __restrict__ As, const T* __restrict__ dO, T* __restrict__ dW2,
-    const int32_t* __restrict__ expert_order, const int32_t* __restrict__ expert_offsets,
-    const int32_t* __restrict__ slot_token, int E, int d, int n, int ntok, int nslot) {
+    float* __restrict__ partials, const int* __restrict__ n_items,
+    const VarlenItem* __restrict__ items, const int32_t* __restrict__ slot_token, int d, int n,
+    int ntok, int nslot) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BM = Cfg::BM, BN = Cfg::BN, EPC = 16 / int(sizeof(T));
   const int TN = d / BN, PT = (n / BM) * TN;
-  int e, tile;
-  if (!varlen_k_tile(blockIdx.x, PT, E, expert_order, &e, &tile)) return;
+  VarlenItem it;
+  int tile;
+  if (!varlen_item(blockIdx.x, PT, n_items, items, &it, &tile)) return;
   const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
-  const int kb = expert_offsets[e], ke = expert_offsets[e + 1];
+  const int kb = it.kb, ke = it.ke;
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
   SlotLoad<Cfg, BM, false> la;
@@ -266,7 +415,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
   acc.init();
   VarlenTail<Cfg, BM, BN> tail{nslabs, ke - kb - (nslabs - 1) * Cfg::BK};
   pipeline<Cfg, false, false>(acc, lds, nslabs, la, lb, tail);
-  store_tile(acc, lds, dW2 + (int64_t(e) * n + i0) * d + j0, d);
+  if (it.pslot < 0)
+    store_tile(acc, lds, dW2 + (int64_t(it.e) * n + i0) * d + j0, d);
+  else
+    store_tile_f32(acc, partials + (int64_t(it.pslot) * n + i0) * d + j0, d);
 }
 
 template <class Cfg>
@@ -305,27 +457,111 @@ void dxt_launch(const LayerArgs& a, const void* dH, const void* W1, void* dXt, h
                      a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
 }
 
-inline unsigned varlen_k_grid(int E, int PT) { return unsigned(8 * ((E + 7) / 8) * PT); }
+// Tile configurations of the two weight-gradient kernels; f(CfgTag<Cfg>{})
+// is called with the one the problem uses (the launchers and the workspace
+// sizing share this choice).
+template <class C>
+struct CfgTag {
+  using type = C;
+};
 
-template <class Cfg>
-void dw1_launch(const LayerArgs& a, const void* X, const void* dH, void* dW1, hipStream_t st) {
-  using T = typename Cfg::T;
-  hipLaunchKernelGGL((k_dw1<Cfg>),
-                     dim3(varlen_k_grid(a.E, (a.d / Cfg::BM) * (2 * a.n / Cfg::BN))),
-                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
-                     static_cast<const T*>(dH), static_cast<T*>(dW1), a.expert_order,
-                     a.expert_offsets, a.slot_token, a.E, a.d, a.n, a.T,
-                     int(a.slot_cap));
+template <class F>
+void dw1_cfg(bool f32, int d, int n, F&& f) {
+  const int n2 = 2 * n;
+  if (f32) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
+  else if (d % 256 == 0 && n2 % 256 == 0) f(CfgTag<GradSquare>{});
+  else if (n2 % 256 == 0) f(CfgTag<GradTall>{});
+  else f(CfgTag<GradSmall>{});
 }
 
-template <class Cfg>
-void dw2_launch(const LayerArgs& a, const void* As, const void* dO, void* dW2, hipStream_t st) {
-  using T = typename Cfg::T;
-  hipLaunchKernelGGL((k_dw2<Cfg>), dim3(varlen_k_grid(a.E, (a.n / Cfg::BM) * (a.d / Cfg::BN))),
-                     dim3(Cfg::kThreads), 0, st, static_cast<const T*>(As),
-                     static_cast<const T*>(dO), static_cast<T*>(dW2), a.expert_order,
-                     a.expert_offsets, a.slot_token, a.E, a.d, a.n, a.T,
-                     int(a.slot_cap));
+template <class F>
+void dw2_cfg(bool f32, int d, int n, F&& f) {
+  if (f32) {
+    if (n % 128 == 0) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
+    else f(CfgTag<TileCfg<float, 64, 128, 2, 2, 3>>{});
+  } else if (n % 256 == 0 && d % 256 == 0) {
+    f(CfgTag<GradSquare>{});
+  } else if (n % 128 == 0 && d % 256 == 0) {
+    f(CfgTag<GradTall>{});
+  } else if (n % 128 == 0) {
+    f(CfgTag<GradSmall>{});
+  } else {
+    f(CfgTag<TileCfg<bf16_t, 64, 128, 2, 2, 3>>{});
+  }
+}
+
+// Chunking of one varlen-K kernel: PT output tiles per expert, chunks of kc
+// rows, and the capacities of its plan.
+struct VarlenDims {
+  int PT, kc, max_items, max_split;
+  int64_t mn;  // elements of one expert's gradient matrix
+};
+
+// kc: one CU's fair share of the kernel's work (in rows of a tile), so that
+// no chunk is longer than what every CU has to do anyway; only experts that
+// would otherwise hold up the end of the kernel are split (each split costs
+// an fp32 partial written and read back).  A multiple of the slab depth, at
+// least four slabs.
+inline VarlenDims varlen_dims(int64_t slot_cap, int E, int PT, int BK, int64_t mn) {
+  int64_t kc = slot_cap * PT / kNumCUs;
+  kc = std::max<int64_t>(kc, 4 * BK);
+  kc = (kc + BK - 1) / BK * BK;
+  VarlenDims v;
+  v.PT = PT;
+  v.kc = int(std::min<int64_t>(kc, 1 << 30));
+  const int64_t chunks = (slot_cap + v.kc - 1) / v.kc;
+  v.max_items = int(E + chunks);  // every expert is one item, plus extra chunks
+  v.max_split = int(2 * chunks);  // a split expert has r > kc rows and < 2 r / kc chunks
+  v.mn = mn;
+  return v;
+}
+
+VarlenDims dw1_dims(bool f32, int d, int n, int E, int64_t slot_cap) {
+  VarlenDims v{};
+  dw1_cfg(f32, d, n, [&](auto tag) {
+    using Cfg = typename decltype(tag)::type;
+    v = varlen_dims(slot_cap, E, (d / Cfg::BM) * (2 * n / Cfg::BN), Cfg::BK, int64_t(d) * 2 * n);
+  });
+  return v;
+}
+
+VarlenDims dw2_dims(bool f32, int d, int n, int E, int64_t slot_cap) {
+  VarlenDims v{};
+  dw2_cfg(f32, d, n, [&](auto tag) {
+    using Cfg = typename decltype(tag)::type;
+    v = varlen_dims(slot_cap, E, (n / Cfg::BM) * (d / Cfg::BN), Cfg::BK, int64_t(n) * d);
+  });
+  return v;
+}
+
+// Workspace of the weight-gradient phase: two plans, then the fp32 partial
+// slabs (shared: dW2 runs after dW1's reduction).
+struct VarlenWs {
+  size_t hdr1, items1, splits1, hdr2, items2, splits2, partials, total;
+  static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
+  static VarlenWs make(const VarlenDims& v1, const VarlenDims& v2, int E) {
+    VarlenWs w;
+    size_t o = 0;
+    w.hdr1 = o; o = align(o + 16);
+    w.items1 = o; o = align(o + size_t(v1.max_items) * sizeof(VarlenItem));
+    w.splits1 = o; o = align(o + size_t(E) * sizeof(VarlenSplit));
+    w.hdr2 = o; o = align(o + 16);
+    w.items2 = o; o = align(o + size_t(v2.max_items) * sizeof(VarlenItem));
+    w.splits2 = o; o = align(o + size_t(E) * sizeof(VarlenSplit));
+    w.partials = o;
+    o += std::max(size_t(v1.max_split) * size_t(v1.mn), size_t(v2.max_split) * size_t(v2.mn)) * 4;
+    w.total = align(o);
+    return w;
+  }
+};
+
+template <class T>
+void reduce_launch(const int* hdr, const VarlenSplit* splits, const float* partials, void* out,
+                   const VarlenDims& v, hipStream_t st) {
+  const int gy = int((v.mn + 2047) / 2048);  // 2048-element units per expert
+  const unsigned grid = unsigned(std::min<int64_t>(int64_t(v.max_split) * gy, 2048));
+  hipLaunchKernelGGL((k_varlen_reduce<T>), dim3(grid), dim3(256), 0, st, hdr, splits, partials,
+                     static_cast<T*>(out), v.mn, gy);
 }
 
 }  // namespace
@@ -345,30 +581,58 @@ hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1,
+size_t varlen_ws_bytes(bool f32, int d, int n, int E, int64_t slot_cap) {
+  return VarlenWs::make(dw1_dims(f32, d, n, E, slot_cap), dw2_dims(f32, d, n, E, slot_cap), E)
+      .total;
+}
+
+hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1, void* vws,
                       hipStream_t st) {
-  const int n2 = 2 * a.n;
-  if (a.f32) dw1_launch<TileCfg<float, 128, 128, 2, 2, 3>>(a, X, dH, dW1, st);
-  else if (a.d % 256 == 0 && n2 % 256 == 0) dw1_launch<GradSquare>(a, X, dH, dW1, st);
-  else if (n2 % 256 == 0) dw1_launch<GradTall>(a, X, dH, dW1, st);
-  else dw1_launch<GradSmall>(a, X, dH, dW1, st);
+  const VarlenDims v1 = dw1_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
+  const VarlenDims v2 = dw2_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
+  const VarlenWs L = VarlenWs::make(v1, v2, a.E);
+  char* w = static_cast<char*>(vws);
+  int* hdr1 = reinterpret_cast<int*>(w + L.hdr1);
+  int* hdr2 = reinterpret_cast<int*>(w + L.hdr2);
+  auto* items1 = reinterpret_cast<VarlenItem*>(w + L.items1);
+  auto* items2 = reinterpret_cast<VarlenItem*>(w + L.items2);
+  auto* splits1 = reinterpret_cast<VarlenSplit*>(w + L.splits1);
+  auto* splits2 = reinterpret_cast<VarlenSplit*>(w + L.splits2);
+  float* partials = reinterpret_cast<float*>(w + L.partials);
+  hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(kPlanThreads), 0, st, a.expert_offsets,
+                     a.expert_order, a.E, v1.kc, v2.kc, hdr1, items1, splits1, hdr2, items2,
+                     splits2);
+  dw1_cfg(a.f32, a.d, a.n, [&](auto tag) {
+    using Cfg = typename decltype(tag)::type;
+    using T = typename Cfg::T;
+    hipLaunchKernelGGL((k_dw1<Cfg>), dim3(unsigned(8 * cdiv(v1.max_items, 8) * v1.PT)),
+                       dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
+                       static_cast<const T*>(dH), static_cast<T*>(dW1), partials, hdr1, items1,
+                       a.slot_token, a.d, a.n, a.T, int(a.slot_cap));
+    reduce_launch<T>(hdr1, splits1, partials, dW1, v1, st);
+  });
   return hipGetLastError();
 }
 
-hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2,
+hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2, void* vws,
                       hipStream_t st) {
-  if (a.f32) {
-    if (a.n % 128 == 0) dw2_launch<TileCfg<float, 128, 128, 2, 2, 3>>(a, As, dO, dW2, st);
-    else dw2_launch<TileCfg<float, 64, 128, 2, 2, 3>>(a, As, dO, dW2, st);
-  } else if (a.n % 256 == 0 && a.d % 256 == 0) {
-    dw2_launch<GradSquare>(a, As, dO, dW2, st);
-  } else if (a.n % 128 == 0 && a.d % 256 == 0) {
-    dw2_launch<GradTall>(a, As, dO, dW2, st);
-  } else if (a.n % 128 == 0) {
-    dw2_launch<GradSmall>(a, As, dO, dW2, st);
-  } else {
-    dw2_launch<TileCfg<bf16_t, 64, 128, 2, 2, 3>>(a, As, dO, dW2, st);
-  }
+  const VarlenDims v1 = dw1_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
+  const VarlenDims v2 = dw2_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
+  const VarlenWs L = VarlenWs::make(v1, v2, a.E);
+  char* w = static_cast<char*>(vws);
+  int* hdr2 = reinterpret_cast<int*>(w + L.hdr2);
+  auto* items2 = reinterpret_cast<VarlenItem*>(w + L.items2);
+  auto* splits2 = reinterpret_cast<VarlenSplit*>(w + L.splits2);
+  float* partials = reinterpret_cast<float*>(w + L.partials);
+  dw2_cfg(a.f32, a.d, a.n, [&](auto tag) {
+    using Cfg = typename decltype(tag)::type;
+    using T = typename Cfg::T;
+    hipLaunchKernelGGL((k_dw2<Cfg>), dim3(unsigned(8 * cdiv(v2.max_items, 8) * v2.PT)),
+                       dim3(Cfg::kThreads), 0, st, static_cast<const T*>(As),
+                       static_cast<const T*>(dO), static_cast<T*>(dW2), partials, hdr2, items2,
+                       a.slot_token, a.d, a.n, a.T, int(a.slot_cap));
+    reduce_launch<T>(hdr2, splits2, partials, dW2, v2, st);
+  });
   return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ struct RouteArgs {
 };
 
 // Everything the grouped GEMMs and aggregation kernels need.
+constexpr int kNumCUs = 256;  // compute units of an MI355X
+
 struct LayerArgs {
   int T, d, n, E;
   int64_t slot_cap, tile_cap;
@@ -55,9 +57,13 @@ hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const v
                      void* dH, void* As, float* dS, hipStream_t st);
 hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
                       hipStream_t st);
-hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1,
+// Varlen-K weight gradients.  `vws` is the weight-gradient workspace of
+// varlen_ws_bytes() bytes (chunk plans and fp32 partial sums); launch_dw1
+// also writes both plans, so it must run first.
+size_t varlen_ws_bytes(bool f32, int d, int n, int E, int64_t slot_cap);
+hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1, void* vws,
                       hipStream_t st);
-hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2,
+hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2, void* vws,
                       hipStream_t st);
 
 }  // namespace moe

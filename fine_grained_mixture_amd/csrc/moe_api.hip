@@ -5,6 +5,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -48,10 +50,14 @@ void sizes_of(const moe_problem* p, moe_sizes_t* s) {
   s->ws_route = moe::RouteWs::make(p->T, p->E).total;
   // forward transients: A [slot_cap, n], Y [slot_cap, d]
   s->ws_fwd = align256(size_t(s->slot_cap * p->n * es)) + align256(size_t(s->slot_cap * p->d * es));
-  // backward transients: dH [slot_cap, 2n], s*A [slot_cap, n], dX~ [slot_cap, d]
+  // backward transients: dH [slot_cap, 2n], s*A [slot_cap, n], then dX~
+  // [slot_cap, d], whose space the weight-gradient phase (chunk plans and
+  // fp32 partial sums) reuses once dX has been aggregated
+  const size_t vw = moe::varlen_ws_bytes(p->dtype == MOE_F32, int(p->d), int(p->n), int(p->E),
+                                         s->slot_cap);
   s->ws_bwd = align256(size_t(s->slot_cap * 2 * p->n * es)) +
               align256(size_t(s->slot_cap * p->n * es)) +
-              align256(size_t(s->slot_cap * p->d * es));
+              std::max(align256(size_t(s->slot_cap * p->d * es)), vw);
 }
 
 bool routing_ok(const moe_routing* r) {
@@ -222,10 +228,10 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
   e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
   if (e != hipSuccess) return MOE_ERR_HIP;
   tr.mark(sm, 3);
-  e = moe::launch_dw1(a, X, dH, dW1, sm);
+  e = moe::launch_dw1(a, X, dH, dW1, dXt, sm);
   if (e != hipSuccess) return MOE_ERR_HIP;
   tr.mark(sm, 4);
-  e = moe::launch_dw2(a, As, dO, dW2, sm);
+  e = moe::launch_dw2(a, As, dO, dW2, dXt, sm);
   tr.mark(sm, 5);
   return hip_status(e);
 }
