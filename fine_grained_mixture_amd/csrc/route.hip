@@ -226,6 +226,8 @@ __global__ __launch_bounds__(kScanThreads) void route_scan(
 // need no memory traffic; KPT == 0 reads the keys from memory in every pass
 // (any T).
 constexpr int kSelThreads = 1024;
+// at most this many keys left under the prefix: rank them directly
+constexpr int kSelFinish = 256;
 
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void route_select(
@@ -240,6 +242,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
   __shared__ uint32_t tot[256];
   __shared__ int sh[kSelThreads / 64 + 1];
   __shared__ int s_digit_info[3];
+  __shared__ uint64_t cand[kSelFinish];  // keys left under the prefix (early finish)
+  __shared__ int s_ncand;
+  __shared__ uint64_t s_thr;
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int f = tc_counts[e], r = counts[e];
   const int nw = (T + 31) >> 5;
@@ -312,6 +317,43 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
         rem = s_digit_info[1];
         cnt_eq = s_digit_info[2];
         __syncthreads();
+        if (KPT > 0 && pass < 7 && cnt_eq <= kSelFinish) {
+          // Few keys left under the prefix: gather them and find the rem-th
+          // largest directly, by counting for each candidate the candidates
+          // above it (and equal to it).
+          if (tid == 0) s_ncand = 0;
+          __syncthreads();
+          if constexpr (KPT > 0) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+              const int t = j * kSelThreads + tid;
+              if (t < T && (kr[j] & mask) == prefix) cand[atomicAdd(&s_ncand, 1)] = kr[j];
+            }
+          }
+          __syncthreads();
+          const int nc = s_ncand;
+          if (tid < nc) {
+            const uint64_t mine = cand[tid];
+            int gt = 0, ge = 0;
+            for (int i = 0; i < nc; ++i) {
+              const uint64_t o = cand[i];
+              gt += o > mine;
+              ge += o >= mine;
+            }
+            if (gt < rem && rem <= ge) {  // every holder of this key writes the same
+              s_thr = mine;
+              s_digit_info[1] = rem - gt;
+              s_digit_info[2] = ge - gt;
+            }
+          }
+          __syncthreads();
+          prefix = s_thr;
+          mask = ~0ull;
+          rem = s_digit_info[1];
+          cnt_eq = s_digit_info[2];
+          __syncthreads();
+          break;
+        }
       }
     }
     // prefix is now the r-th largest key; `rem` of the cnt_eq equal keys are
