@@ -79,6 +79,7 @@ __device__ __forceinline__ float unordered_f32(uint32_t o) {
 constexpr int kTopkLanes = 16;
 constexpr int kTopkTokens = 32;
 constexpr int kTopkThreads = kTopkLanes * kTopkTokens;
+constexpr int kStageE = 128;  // experts per LDS staging group of the key write-out
 
 template <int EPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk(
@@ -87,6 +88,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
     uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e, uint32_t* __restrict__ bits_t) {
   static_assert(EPL >= 1 && EPL <= 64, "experts per lane");
   __shared__ uint32_t sbits[1024];
+  __shared__ uint64_t stage[kStageE][kTopkTokens + 1];
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kTopkThreads) sbits[i] = 0u;
   {
@@ -132,28 +134,43 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
       atomicOr(&sbits[eb], 1u << tl);
     }
   }
+  // softmax in fp64: each exponential is evaluated once and kept, and the
+  // normalisation is one reciprocal
+  double ex[EPL];
   double z = 0.0;
-  if (valid) {
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = sub + kTopkLanes * j;
-      if (e < E) z += exp(double(row[e]) - m);
-    }
+  for (int j = 0; j < EPL; ++j) {
+    const int e = sub + kTopkLanes * j;
+    ex[j] = (valid && e < E) ? exp(double(row[e]) - m) : 0.0;
+    z += ex[j];
   }
 #pragma unroll
   for (int o = 1; o < kTopkLanes; o <<= 1) z += __shfl_xor(z, o, 64);
-  if (valid) {
+  const double rz = 1.0 / z;
+  __syncthreads();  // sbits complete; stage below reuses nothing of it
+  // Keys go out expert-major (row e holds all T tokens): staged in LDS per
+  // group of kStageE experts so that each row receives the block's 32
+  // consecutive tokens as one 256-byte run.
+  const int t0 = blockIdx.x * kTopkTokens;
+  const int ntok = min(kTopkTokens, T - t0);
+#pragma unroll
+  for (int g = 0; g < (EPL * kTopkLanes + kStageE - 1) / kStageE; ++g) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = sub + kTopkLanes * j;
-      if (e < E) {
-        const double p = exp(double(row[e]) - m) / z;
-        keys[int64_t(e) * T + t] =
-            (((taken >> j) & 1ull) << 63) | uint64_t(__double_as_longlong(p));
+      if (e / kStageE == g && e < E) {
+        const double pe = ex[j] * rz;
+        stage[e % kStageE][tl] = (((taken >> j) & 1ull) << 63) | uint64_t(__double_as_longlong(pe));
       }
     }
+    __syncthreads();
+    const int ne = min(kStageE, E - g * kStageE);
+    for (int i = tid; i < ne * kTopkTokens; i += kTopkThreads) {
+      const int el = i / kTopkTokens, tt = i % kTopkTokens;
+      if (tt < ntok) keys[int64_t(g * kStageE + el) * T + t0 + tt] = stage[el][tt];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int nw = (T + 31) >> 5;
   for (int e = tid; e < E; e += kTopkThreads) bits_e[int64_t(e) * nw + blockIdx.x] = sbits[e];
 }
