@@ -171,7 +171,7 @@ struct KLoad {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       dma16(rs, off[i] + uint32_t(s * KB), tile + (i * Cfg::NW + w) * 1024);
-  }
+  }  __device__ __forceinline__ void next(int) const {}
 };
 
 // MN-major operand with a fixed row stride (weights): row k of slab s is at
@@ -207,27 +207,37 @@ struct MNLoad {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       dma16(rs, off[i] + uint32_t(s) * step, tile + (i * Cfg::NW + w) * 1024);
-  }
+  }  __device__ __forceinline__ void next(int) const {}
 };
 
 // MN-major operand whose rows are an expert's slots (varlen-K): row k of
 // slab s is slot kb + s*BK + k, read from source row idx[slot] (GATHER) or
 // row slot of a buffer of `bytes` bytes at `base`; slots past the expert's
-// end read its last slot and are zeroed in LDS afterwards.  The gather
-// indices are wave-uniform per row and are read with scalar loads, so they
-// do not count against the DMA wait counter.
+// end read its last slot and are zeroed in LDS afterwards.  Each lane's
+// source rows are fetched one issue ahead (vector loads that land while the
+// previous slab is multiplied), so no DMA waits for its gather index.
+// issue(s) then next(s) must be called for s = 0, 1, 2, ... in order.
 template <class Cfg, int COLS, bool GATHER>
 struct SlotLoad {
   using T = typename Cfg::T;
   static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
   static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
   static constexpr int RPI = 64 / CH;  // tile rows per DMA instruction
-  static_assert(NI >= 1 && RPI >= 1 && (!GATHER || RPI <= 4), "tile size");
+  static_assert(NI >= 1 && RPI >= 1, "tile size");
   rsrc_t rs;
   const int32_t* idx;
   uint32_t ld_bytes;
   uint32_t colb[NI];
+  mutable int row[NI];  // source rows of the next issue
   int kb, klast, w, sub;
+
+  __device__ __forceinline__ void fetch(int s) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int slot = min(kb + s * Cfg::BK + (i * Cfg::NW + w) * RPI + sub, klast);
+      row[i] = GATHER ? idx[slot] : slot;
+    }
+  }
 
   template <class ColBytes>
   __device__ __forceinline__ void init(const void* base, uint32_t bytes, uint32_t ldb,
@@ -237,7 +247,7 @@ struct SlotLoad {
     idx = index;
     ld_bytes = ldb;
     kb = kbeg;
-    klast = kend - 1;
+    klast = max(kend - 1, kbeg);
     w = wave_id();
     const int L = threadIdx.x & 63;
     sub = L / CH;
@@ -247,25 +257,15 @@ struct SlotLoad {
       const int k = q / CH, pos = q % CH;
       colb[i] = uint32_t(col_bytes(pos ^ mswz<CH>(k)));
     }
+    fetch(0);
   }
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int k0 = kb + s * Cfg::BK + (i * Cfg::NW + w) * RPI;  // wave-uniform
-      int row;
-      if constexpr (GATHER) {
-        int r[RPI];
-#pragma unroll
-        for (int q = 0; q < RPI; ++q) r[q] = idx[min(k0 + q, klast)];
-        row = r[0];
-#pragma unroll
-        for (int q = 1; q < RPI; ++q) row = (sub == q) ? r[q] : row;
-      } else {
-        row = min(k0 + sub, klast);
-      }
-      dma16(rs, uint32_t(row) * ld_bytes + colb[i], tile + (i * Cfg::NW + w) * 1024);
-    }
+    for (int i = 0; i < NI; ++i)
+      dma16(rs, uint32_t(row[i]) * ld_bytes + colb[i], tile + (i * Cfg::NW + w) * 1024);
   }
+  // after both operands of slab s have been issued: rows of slab s + 1
+  __device__ __forceinline__ void next(int s) const { fetch(s + 1); }
 };
 
 // Zero rows [valid, BK) of an MN-major tile of COLS elements (tail slab of a
@@ -409,6 +409,8 @@ __device__ __forceinline__ void pipeline_step(Accum<Cfg>& acc, const char* __res
   if (issue) {
     la.issue(s_next, nxt);
     lb.issue(s_next, nxt + Cfg::A_BYTES);
+    la.next(s_next);
+    lb.next(s_next);
   }
   tail(s, const_cast<char*>(cur));
   acc.template slab<AK, BKM>(cur, cur + Cfg::A_BYTES);
@@ -433,6 +435,8 @@ __device__ __forceinline__ void pipeline(Accum<Cfg>& acc, char* lds, int nslabs,
       char* sp = lds + st * Cfg::STAGE_BYTES;
       la.issue(st, sp);
       lb.issue(st, sp + Cfg::A_BYTES);
+      la.next(st);
+      lb.next(st);
     }
   }
   for (int s = 0; s < nslabs; ++s) {
