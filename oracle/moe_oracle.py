@@ -38,8 +38,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TC = 0  # vanilla top-K token choice
-TR = 1  # token rounding
+TC = 0             # vanilla top-K token choice
+TR = 1             # token rounding, nearest multiple of M_tile (the default)
+TR_UP = 2          # token rounding, always to the multiple above
+TR_DOWN = 3        # token rounding, always to the multiple below
+TR_STOCHASTIC = 4  # token rounding, up with probability (f - lo) / M_tile
+TR_MODES = (TR, TR_UP, TR_DOWN, TR_STOCHASTIC)
 
 
 # --------------------------------------------------------------------------
@@ -75,21 +79,43 @@ def topk_token_choice(logits, K):
     return order[:, :K].astype(np.int64)
 
 
-def round_counts(f, M, T, mode):
+def round_counts(f, M, T, mode, rand_u32=None):
     """Per-expert token counts after the rounding subroutine of token rounding.
 
     Notes, key design 1: with lo = the largest multiple of M not above f_e
-    and hi = the smallest multiple not below it, the expert is padded up to
-    hi when (hi - f_e) < (f_e - lo) and otherwise dropped down to lo.  An
-    equal gap therefore rounds down.  A pad needs hi distinct tokens, so hi is
-    only taken when hi <= T.  Under TC the counts are left as they are.
+    and hi = the smallest multiple not below it, the default subroutine pads
+    the expert up to hi when (hi - f_e) < (f_e - lo) and otherwise drops it to
+    lo, so an equal gap rounds down.  The notes' loss function / training
+    strategy section reports that the choice of subroutine matters little, and
+    key design 1 that the expected total stays that of token choice; the other
+    subroutines built here are the plain readings of those remarks:
+      * TR_UP:   always hi;
+      * TR_DOWN: always lo;
+      * TR_STOCHASTIC: hi with probability (f_e - lo) / M, so E[r_e] = f_e.
+        The draw is an input, one uint32 u_e per expert, and the decision is
+        taken in integers: hi iff u_e * M < (f_e - lo) * 2**32.
+    A pad needs hi distinct tokens, so hi is only taken when hi <= T.  Under
+    TC the counts are left as they are.
     """
     f = np.asarray(f, dtype=np.int64)
     if mode == TC:
         return f.copy()
     lo = (f // M) * M
     hi = np.where(f % M == 0, f, lo + M)
-    up = ((hi - f) < (f - lo)) & (hi <= T)
+    if mode == TR:
+        up = (hi - f) < (f - lo)
+    elif mode == TR_UP:
+        up = hi > f
+    elif mode == TR_DOWN:
+        up = np.zeros(f.shape, dtype=bool)
+    elif mode == TR_STOCHASTIC:
+        if rand_u32 is None:
+            raise ValueError("stochastic rounding needs one uint32 draw per expert")
+        u = np.asarray(rand_u32, dtype=np.uint64)
+        up = u * np.uint64(M) < (f - lo).astype(np.uint64) << np.uint64(32)
+    else:
+        raise ValueError(f"unknown routing mode {mode}")
+    up = up & (hi <= T)
     return np.where(up, hi, lo)
 
 
@@ -133,10 +159,11 @@ class Routing:
         return int(self.expert_offsets[-1])
 
 
-def route(logits, K, M, mode):
+def route(logits, K, M, mode, rand_u32=None):
     """Top-K token choice, optionally followed by token rounding (notes,
     key design 1; abstract).  Gate weights are the softmax probabilities of
-    the kept (token, expert) pairs, not renormalised."""
+    the kept (token, expert) pairs, not renormalised.  `rand_u32` holds the
+    per-expert draws of stochastic rounding (ignored by the other modes)."""
     l32 = np.asarray(logits, dtype=np.float32)
     T, E = l32.shape
     p = softmax_probs(l32)
@@ -144,7 +171,7 @@ def route(logits, K, M, mode):
     is_tc = np.zeros((T, E), dtype=bool)
     is_tc[np.arange(T)[:, None], topk] = True
     f = is_tc.sum(axis=0).astype(np.int64)
-    r = round_counts(f, M, T, mode)
+    r = round_counts(f, M, T, mode, rand_u32)
     if mode == TC:
         sel = [np.nonzero(is_tc[:, e])[0].astype(np.int64) for e in range(E)]
     else:

@@ -32,3 +32,14 @@ def worked_example():
             rows.append([float(v) for v in line.split()])
     out["logits"] = np.array(rows, dtype=np.float32)
     return out
+
+
+def rounding_variant_cases():
+    """(section, row) pairs of tr_rounding_variants.txt."""
+    out, section = [], None
+    for line in _lines("tr_rounding_variants.txt"):
+        if line in ("updown", "stochastic"):
+            section = line
+            continue
+        out.append((section, tuple(int(v) for v in line.split())))
+    return out

@@ -12,7 +12,7 @@ import pytest
 
 from oracle import moe_oracle as orc
 from fine_grained_mixture_amd.inputs import SHAPES, make_layer_inputs
-from tests.golden_io import rounding_cases, worked_example
+from tests.golden_io import rounding_cases, rounding_variant_cases, worked_example
 
 
 def brute_topk(row, K):
@@ -88,16 +88,24 @@ def _tr_reference_sets(p, is_tc, r):
     return sets
 
 
-def check_tr_invariants(logits, K, M):
+def check_tr_invariants(logits, K, M, mode=orc.TR, rand=None):
     T, E = logits.shape
     tc = orc.route(logits, K, M, orc.TC)
-    tr = orc.route(logits, K, M, orc.TR)
+    tr = orc.route(logits, K, M, mode, rand)
     f, r = tr.tc_counts, tr.counts
     assert np.array_equal(f, tc.counts)
     assert np.all(r % M == 0)                       # multiples of the tile
     assert np.all(np.abs(r - f) < M)                # within one tile of TC
-    assert np.all(2 * np.abs(r - f) <= M)           # nearest rounding
-    assert abs(int(r.sum()) - int(f.sum())) <= E * M // 2
+    lo = (f // M) * M
+    hi = np.where(f % M == 0, f, lo + M)
+    assert np.all((r == lo) | (r == hi))            # one of the two neighbours
+    if mode == orc.TR:
+        assert np.all(2 * np.abs(r - f) <= M)       # nearest rounding
+        assert abs(int(r.sum()) - int(f.sum())) <= E * M // 2
+    elif mode == orc.TR_UP:
+        assert np.all((r >= f) | (hi > T))
+    elif mode == orc.TR_DOWN:
+        assert np.all(r <= f)
     p = tr.probs
     is_tc = np.zeros((T, E), bool)
     is_tc[np.arange(T)[:, None], tr.topk_ids] = True
@@ -190,3 +198,58 @@ def test_tr_equal_scores_go_to_lower_token():
     tr = orc.route(np.array(rows, np.float32), K=1, M=4, mode=orc.TR)
     assert list(tr.counts) == [4, 4]
     assert tr.slot_token[:4].tolist() == [0, 1, 2, 3]
+
+
+# ---- rounding subroutines other than the nearest one -----------------------
+
+@pytest.mark.parametrize("section,row", rounding_variant_cases())
+def test_rounding_variants_golden(section, row):
+    if section == "updown":
+        f, M, T, up, down = row
+        assert int(orc.round_counts([f], M, T, orc.TR_UP)[0]) == up
+        assert int(orc.round_counts([f], M, T, orc.TR_DOWN)[0]) == down
+    else:
+        f, M, T, u, expected = row
+        assert int(orc.round_counts([f], M, T, orc.TR_STOCHASTIC, [u])[0]) == expected
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 128])
+def test_stochastic_rounding_expectation_is_exact(M):
+    # Over the M evenly spaced draws u_j = floor(j 2^32 / M), exactly f - lo
+    # of them round up, so the mean count is f itself (key design 1: the
+    # expected total count is that of token choice).
+    T = 1 << 20
+    u = np.array([(j << 32) // M for j in range(M)], dtype=np.uint64)
+    for f in list(range(0, 3 * M + 1)) + [5513, 1000]:
+        r = np.array([int(orc.round_counts([f], M, T, orc.TR_STOCHASTIC, [x])[0]) for x in u])
+        lo = (f // M) * M
+        assert np.all((r == lo) | (r == lo + M))
+        assert int((r > lo).sum()) == f - lo
+        assert r.sum() == f * M
+
+
+def test_rounding_modes_need_their_draws():
+    with pytest.raises(ValueError):
+        orc.round_counts([5], 4, 100, orc.TR_STOCHASTIC)
+    with pytest.raises(ValueError):
+        orc.round_counts([5], 4, 100, 99)
+
+
+@pytest.mark.parametrize("mode", [orc.TR_UP, orc.TR_DOWN, orc.TR_STOCHASTIC])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_variant_invariants_random(mode, seed):
+    rng = np.random.default_rng(100 + seed)
+    T, E, K, M = 300, 12, 3, 16
+    logits = (rng.standard_normal((T, E)) + rng.standard_normal(E)).astype(np.float32)
+    rand = rng.integers(0, 1 << 32, size=E, dtype=np.uint64)
+    check_tr_invariants(logits, K, M, mode, rand)
+
+
+@pytest.mark.parametrize("mode", [orc.TR_UP, orc.TR_DOWN, orc.TR_STOCHASTIC])
+def test_variants_with_m1_equal_tc(mode):
+    rng = np.random.default_rng(7)
+    logits = rng.standard_normal((70, 9)).astype(np.float32)
+    tc = orc.route(logits, 3, 1, orc.TC)
+    tr = orc.route(logits, 3, 1, mode, np.zeros(9, np.uint64))
+    assert np.array_equal(tc.slot_token, tr.slot_token)
+    assert np.array_equal(tc.expert_offsets, tr.expert_offsets)
