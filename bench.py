@@ -11,7 +11,7 @@ between its launches; `cpu_baseline` times the fp64 oracle on a bounded
 sample of the same workload (a subset of the experts) on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 7b]
-                       [--mode tr|tc] [--no-cpu-baseline]
+                       [--mode tc|tr|tr_up|tr_down|tr_stochastic] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -28,7 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from fine_grained_mixture_amd import moe  # noqa: E402
-from fine_grained_mixture_amd.inputs import SHAPES, make_layer_inputs  # noqa: E402
+from fine_grained_mixture_amd.inputs import (SHAPES, make_layer_inputs,  # noqa: E402
+                                             make_round_rand, round_rand_tensor)
 from fine_grained_mixture_amd.profiling import kernel_model, read_traffic  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -68,7 +69,9 @@ def cpu_baseline(sh, inp, mode, target_s=15.0):
     a = {k: v.float().numpy().astype(np.float64) for k, v in inp.items() if k != "logits"}
     logits = inp["logits"].numpy()
     t0 = time.perf_counter()
-    rt = orc.route(logits, sh.K, sh.M, orc.TR if mode == "tr" else orc.TC)
+    modes = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
+             "tr_stochastic": orc.TR_STOCHASTIC}
+    rt = orc.route(logits, sh.K, sh.M, modes[mode], make_round_rand(sh.E, 0))
     t_route = time.perf_counter() - t0
     # Grow the expert sample until the timed fwd+bwd takes a few seconds.
     order = np.argsort(-rt.counts, kind="stable")
@@ -104,7 +107,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
-    ap.add_argument("--mode", default="tr", choices=["tr", "tc"])
+    ap.add_argument("--mode", default="tr", choices=sorted(moe.ROUTE_MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (known HBM "
@@ -131,6 +134,7 @@ def main():
     sh = SHAPES[args.config]
     inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)
     X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
+    rr = round_rand_tensor(make_round_rand(sh.E, 0)).to(dev)  # stochastic rounding draws
     p = moe.problem(sh.T, sh.d, sh.n, sh.E, sh.K, sh.M, torch.bfloat16, args.mode)
     sz = moe.sizes(p)
     rt = moe.alloc_routing(p, dev)
@@ -154,7 +158,7 @@ def main():
 
     def step(ev=None):
         e_r, e_f, e_b = ev if ev else (None, None, None)
-        moe.route(p, lg, rt=rt, ws=ws_r, stream=stream, events=e_r)
+        moe.route(p, lg, rt=rt, ws=ws_r, stream=stream, events=e_r, round_rand=rr)
         moe.forward(p, X, W1, W2, rt, out=(O, H), ws=ws_f, stream=stream, events=e_f)
         moe.backward(p, dO, X, H, W1, W2, rt, out=grads, ws=ws_b, stream=stream, events=e_b)
 

@@ -19,8 +19,9 @@ struct TraceHook {
 };
 
 struct RouteArgs {
-  int T, E, K, M, mode;
+  int T, E, K, M, mode;  // mode: moe_route_mode
   const float* logits;
+  const uint32_t* round_rand;  // [E] draws of stochastic rounding, else null
   int32_t *tc_counts, *counts, *expert_offsets, *expert_order, *topk_ids;
   int32_t* slot_token;
   float* slot_weight;

@@ -26,7 +26,7 @@ int check_problem(const moe_problem* p) {
     return MOE_ERR_INVALID;
   if (p->K > p->E) return MOE_ERR_INVALID;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_F32) return MOE_ERR_INVALID;
-  if (p->mode != MOE_ROUTE_TC && p->mode != MOE_ROUTE_TR) return MOE_ERR_INVALID;
+  if (p->mode < MOE_ROUTE_TC || p->mode > MOE_ROUTE_TR_STOCHASTIC) return MOE_ERR_INVALID;
   if (p->K > 32 || p->E > 1024 || p->M_tile > 1024) return MOE_ERR_UNSUPPORTED;
   if (p->d % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (p->n != 64 && p->n != 128 && p->n != 256 && p->n != 384) return MOE_ERR_UNSUPPORTED;
@@ -135,11 +135,15 @@ int moe_sizes(const moe_problem* p, moe_sizes_t* out) {
   return MOE_OK;
 }
 
-int moe_route(const moe_problem* p, const float* logits, const moe_routing* r, void* ws,
-              size_t ws_bytes, void* stream, const moe_trace* trace) {
+int moe_route(const moe_problem* p, const float* logits, const uint32_t* round_rand,
+              const moe_routing* r, void* ws, size_t ws_bytes, void* stream,
+              const moe_trace* trace) {
   int st = check_problem(p);
   if (st != MOE_OK) return st;
   if (!aligned16(logits) || !routing_ok(r) || !aligned16(ws) || !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  if (p->mode == MOE_ROUTE_TR_STOCHASTIC &&
+      (!round_rand || reinterpret_cast<uintptr_t>(round_rand) % 4 != 0))
     return MOE_ERR_INVALID;
   moe_sizes_t s;
   sizes_of(p, &s);
@@ -151,6 +155,7 @@ int moe_route(const moe_problem* p, const float* logits, const moe_routing* r, v
   a.M = int(p->M_tile);
   a.mode = p->mode;
   a.logits = logits;
+  a.round_rand = p->mode == MOE_ROUTE_TR_STOCHASTIC ? round_rand : nullptr;
   a.tc_counts = r->tc_counts;
   a.counts = r->counts;
   a.expert_offsets = r->expert_offsets;

@@ -21,6 +21,7 @@
 //                 64-bit keys), slot list in token order, gate weights
 //   route_tcount  per block of tokens: number of slots
 //   route_tslots  per token: CSR offset and its slots in ascending expert order
+#include "moe.h"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -178,7 +179,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
 // Per expert: f_e = number of set bits in its row of the token-choice bitmap,
 // and the rounded count r_e.
 __global__ __launch_bounds__(256) void route_count(
-    int T, int M, int mode, const uint32_t* __restrict__ bits_e, int32_t* __restrict__ tc_counts,
+    int T, int M, int mode, const uint32_t* __restrict__ round_rand,
+    const uint32_t* __restrict__ bits_e, int32_t* __restrict__ tc_counts,
     int32_t* __restrict__ counts) {
   __shared__ int sh[256 / 64 + 1];
   const int e = blockIdx.x, nw = (T + 31) >> 5;
@@ -189,10 +191,15 @@ __global__ __launch_bounds__(256) void route_count(
   block_excl_scan(c, sh, &f);
   if (threadIdx.x == 0) {
     int r = f;
-    if (mode == 1) {
+    if (mode != MOE_ROUTE_TC) {
       const int lo = (f / M) * M;
       const int hi = (f % M == 0) ? f : lo + M;
-      r = ((hi - f) < (f - lo) && hi <= T) ? hi : lo;
+      bool up;
+      if (mode == MOE_ROUTE_TR) up = (hi - f) < (f - lo);
+      else if (mode == MOE_ROUTE_TR_UP) up = hi > f;
+      else if (mode == MOE_ROUTE_TR_DOWN) up = false;
+      else up = uint64_t(round_rand[e]) * uint64_t(M) < (uint64_t(f - lo) << 32);
+      r = (up && hi <= T) ? hi : lo;
     }
     tc_counts[e] = f;
     counts[e] = r;
@@ -531,8 +538,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
 #undef MOE_TOPK
   }
   tr.mark(st, 1);
-  hipLaunchKernelGGL(route_count, dim3(E), dim3(256), 0, st, T, a.M, a.mode, bits_e, a.tc_counts,
-                     a.counts);
+  hipLaunchKernelGGL(route_count, dim3(E), dim3(256), 0, st, T, a.M, a.mode, a.round_rand, bits_e,
+                     a.tc_counts, a.counts);
   tr.mark(st, 2);
   hipLaunchKernelGGL(route_scan, dim3(1), dim3(kScanThreads), 0, st, a.counts, E,
                      a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row, a.totals);

@@ -106,3 +106,16 @@ def make_layer_inputs(shape: LayerShape | str, dtype=torch.bfloat16, seed=0,
         "logits": torch.from_numpy(np.ascontiguousarray(logits, dtype=f32)),
         "dO": _cast(dO, dtype),
     }
+
+
+def make_round_rand(E: int, seed: int = 0) -> np.ndarray:
+    """The per-expert uniform draws of stochastic token rounding: E values in
+    [0, 2**32) from numpy PCG64 seeded with (seed, 0x52D), as uint64.  The
+    device takes the same values as 32-bit words (``round_rand_tensor``)."""
+    rng = np.random.default_rng([seed, 0x52D])
+    return rng.integers(0, 1 << 32, size=E, dtype=np.uint64)
+
+
+def round_rand_tensor(rand: np.ndarray) -> torch.Tensor:
+    """[E] int32 CPU tensor holding the bits of the uint32 draws."""
+    return torch.from_numpy(np.ascontiguousarray(rand.astype(np.uint32).view(np.int32)))

@@ -18,7 +18,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 MOE_BF16, MOE_F32 = 0, 1
-MOE_ROUTE_TC, MOE_ROUTE_TR = 0, 1
+MOE_ROUTE_TC, MOE_ROUTE_TR, MOE_ROUTE_TR_UP, MOE_ROUTE_TR_DOWN, MOE_ROUTE_TR_STOCHASTIC = range(5)
+ROUTE_MODES = {"tc": MOE_ROUTE_TC, "tr": MOE_ROUTE_TR, "tr_up": MOE_ROUTE_TR_UP,
+               "tr_down": MOE_ROUTE_TR_DOWN, "tr_stochastic": MOE_ROUTE_TR_STOCHASTIC}
 TILE_M = 128
 
 ROUTE_KERNELS = ("route_topk", "route_count", "route_scan", "route_select", "route_tcount",
@@ -70,7 +72,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, V, S = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
     L.moe_sizes.argtypes = [P(Problem), P(Sizes)]
-    L.moe_route.argtypes = [P(Problem), V, P(RoutingStruct), V, S, V, P(Trace)]
+    L.moe_route.argtypes = [P(Problem), V, V, P(RoutingStruct), V, S, V, P(Trace)]
     L.moe_fwd.argtypes = [P(Problem), V, V, V, P(RoutingStruct), V, V, V, S, V, P(Trace)]
     L.moe_bwd.argtypes = [P(Problem), V, V, V, V, V, P(RoutingStruct), V, V, V, V, V, S, V,
                           P(Trace)]
@@ -90,7 +92,7 @@ def _check(status):
 
 def problem(T, d, n, E, K, M_tile, dtype=torch.bfloat16, mode="tr") -> Problem:
     dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[dtype]
-    md = {"tc": MOE_ROUTE_TC, "tr": MOE_ROUTE_TR}[mode]
+    md = ROUTE_MODES[mode]
     return Problem(T, d, n, E, K, M_tile, dt, md)
 
 
@@ -174,13 +176,20 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 def route(p: Problem, logits: torch.Tensor, rt: Routing | None = None, ws=None, stream=None,
-          events=None) -> Routing:
-    """moe_route: top-K token choice, optionally token rounding."""
+          events=None, round_rand: torch.Tensor | None = None) -> Routing:
+    """moe_route: top-K token choice, optionally token rounding.  `round_rand`
+    ([E] int32 on the device, read as uint32 draws) is needed by the
+    stochastic rounding mode and ignored by the others."""
     lg = _dev(logits, "logits", torch.float32, (p.T, p.E))
+    rr = None
+    if p.mode == MOE_ROUTE_TR_STOCHASTIC:
+        if round_rand is None:
+            raise MoEError("stochastic token rounding needs round_rand ([E] draws)")
+        rr = _dev(round_rand, "round_rand", torch.int32, (p.E,))
     rt = rt if rt is not None else alloc_routing(p, logits.device)
     ws = ws if ws is not None else workspace(sizes(p).ws_route, logits.device)
     tr = _trace(events)
-    _check(lib().moe_route(ctypes.byref(p), lg, ctypes.byref(rt.struct),
+    _check(lib().moe_route(ctypes.byref(p), lg, rr, ctypes.byref(rt.struct),
                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
                            ctypes.byref(tr) if tr else None))
     return rt

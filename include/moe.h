@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Rows per M tile of the grouped GEMMs; the tile schedule in moe_routing is
  * expressed in these units. */
@@ -66,8 +66,11 @@ typedef enum {
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
 
 typedef enum {
-  MOE_ROUTE_TC = 0, /* vanilla top-K token choice                            */
-  MOE_ROUTE_TR = 1  /* token choice followed by token rounding to M_tile     */
+  MOE_ROUTE_TC = 0,            /* vanilla top-K token choice                 */
+  MOE_ROUTE_TR = 1,            /* token rounding, nearest multiple of M_tile */
+  MOE_ROUTE_TR_UP = 2,         /* token rounding, always up (hi)             */
+  MOE_ROUTE_TR_DOWN = 3,       /* token rounding, always down (lo)           */
+  MOE_ROUTE_TR_STOCHASTIC = 4  /* token rounding, up w.p. (f - lo) / M_tile  */
 } moe_route_mode;
 
 typedef struct {
@@ -133,15 +136,27 @@ int moe_sizes(const moe_problem *p, moe_sizes_t *out);
  *   TopK(t) = the K largest fp32 logits, equal logits to the lower expert;
  *   f_e     = number of tokens whose TopK holds e;
  *   TC:  r_e = f_e and expert e keeps exactly those tokens;
- *   TR:  lo/hi = the multiples of M_tile just below/above f_e; r_e = hi when
- *        hi - f_e < f_e - lo and hi <= T, else lo; expert e keeps the first
+ *   TR*: lo/hi = the multiples of M_tile just below/above f_e, and r_e is
+ *        TR            hi when hi - f_e < f_e - lo, else lo (the notes' rule);
+ *        TR_UP         hi;
+ *        TR_DOWN       lo;
+ *        TR_STOCHASTIC hi when round_rand[e] * M_tile < (f_e - lo) * 2^32
+ *                      (integer comparison), else lo, so E[r_e] = f_e
+ *                      (notes, key design 1: the expected total count is
+ *                      that of token choice; the loss function / training
+ *                      strategy section: the subroutine matters little);
+ *        every TR mode takes hi only when hi <= T.  Expert e keeps the first
  *        r_e tokens ordered by (e in TopK(t), p[t,e]) descending, equal keys
  *        to the lower token;
  *   s = p[t,e] for every kept pair (no renormalisation).
+ * round_rand: [E] uint32 device buffer of uniform draws, one per expert,
+ * owned by the caller; required (4-byte aligned) for TR_STOCHASTIC, ignored
+ * (may be NULL) otherwise.  MOE_ERR_INVALID if required and NULL.
  * ws: at least sizes.ws_route bytes.  Writes every field of `r`.
  */
-int moe_route(const moe_problem *p, const float *logits, const moe_routing *r,
-              void *ws, size_t ws_bytes, void *stream, const moe_trace *trace);
+int moe_route(const moe_problem *p, const float *logits, const uint32_t *round_rand,
+              const moe_routing *r, void *ws, size_t ws_bytes, void *stream,
+              const moe_trace *trace);
 
 /*
  * Forward (notes, method > overall framework; key design 2).  For every

@@ -33,7 +33,7 @@ def test_exports_every_declared_function():
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -62,7 +62,7 @@ def test_sizes_fp32_doubles_transients():
 
 @pytest.mark.parametrize("field,value,status", [
     ("T", 0, INVALID), ("d", -128, INVALID), ("K", 9, INVALID), ("M_tile", 0, INVALID),
-    ("dtype", 5, INVALID), ("mode", 2, INVALID), ("K", 33, UNSUPPORTED),
+    ("dtype", 5, INVALID), ("mode", 5, INVALID), ("mode", -1, INVALID), ("K", 33, UNSUPPORTED),
     ("d", 192, UNSUPPORTED), ("n", 96, UNSUPPORTED), ("n", 512, UNSUPPORTED),
     ("E", 2048, UNSUPPORTED), ("M_tile", 4096, UNSUPPORTED), ("T", 1 << 26, UNSUPPORTED),
 ])
@@ -84,13 +84,30 @@ def test_route_validation_before_launch():
     p = moe.problem(256, 128, 64, 8, 2, 16)
     need = moe.sizes(p).ws_route
     r = _routing()
-    assert L.moe_route(ctypes.byref(p), None, ctypes.byref(r), FAKE, need, None, None) == INVALID
-    assert L.moe_route(ctypes.byref(p), FAKE + 4, ctypes.byref(r), FAKE, need, None, None) == INVALID
-    assert L.moe_route(ctypes.byref(p), FAKE, ctypes.byref(_routing(0)), FAKE, need, None,
+    rr = ctypes.byref(r)
+    assert L.moe_route(ctypes.byref(p), None, None, rr, FAKE, need, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(p), FAKE + 4, None, rr, FAKE, need, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(p), FAKE, None, ctypes.byref(_routing(0)), FAKE, need, None,
                        None) == INVALID
-    assert L.moe_route(ctypes.byref(p), FAKE, ctypes.byref(r), FAKE, need - 1, None,
+    assert L.moe_route(ctypes.byref(p), FAKE, None, rr, FAKE, need - 1, None,
                        None) == WORKSPACE
-    assert L.moe_route(None, FAKE, ctypes.byref(r), FAKE, need, None, None) == INVALID
+    assert L.moe_route(None, FAKE, None, rr, FAKE, need, None, None) == INVALID
+
+
+def test_stochastic_rounding_needs_draws():
+    L = moe.lib()
+    p = moe.problem(256, 128, 64, 8, 2, 16, mode="tr_stochastic")
+    need = moe.sizes(p).ws_route
+    rr = ctypes.byref(_routing())
+    assert L.moe_route(ctypes.byref(p), FAKE, None, rr, FAKE, need, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE + 2, rr, FAKE, need, None, None) == INVALID
+    # with valid draws the next check is the workspace size (nothing is
+    # launched); the other modes never look at the draws
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, rr, FAKE, need - 1, None, None) == WORKSPACE
+    for mode in ("tr_up", "tr_down"):
+        q = moe.problem(256, 128, 64, 8, 2, 16, mode=mode)
+        assert L.moe_route(ctypes.byref(q), FAKE, None, rr, FAKE, need - 1, None,
+                           None) == WORKSPACE
 
 
 def test_fwd_bwd_validation_before_launch():
@@ -119,5 +136,5 @@ def test_null_trace_event_rejected():
     need = moe.sizes(p).ws_route
     ev = (ctypes.c_void_p * 7)(*([FAKE] * 6 + [None]))
     tr = moe.Trace(ev, 7)
-    assert L.moe_route(ctypes.byref(p), FAKE, ctypes.byref(_routing()), FAKE, need, None,
+    assert L.moe_route(ctypes.byref(p), FAKE, None, ctypes.byref(_routing()), FAKE, need, None,
                        ctypes.byref(tr)) == INVALID

@@ -18,7 +18,8 @@ import pytest
 import torch
 
 from fine_grained_mixture_amd import moe
-from fine_grained_mixture_amd.inputs import SHAPES, LayerShape, make_layer_inputs
+from fine_grained_mixture_amd.inputs import (SHAPES, LayerShape, make_layer_inputs,
+                                             make_round_rand, round_rand_tensor)
 from oracle import moe_oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -36,6 +37,12 @@ EXTRA = {
     "m1": LayerShape("m1", 512, 256, 64, 16, 2, 1, "fan_in", "iid"),
 }
 TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
+ORC_MODE = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
+            "tr_stochastic": orc.TR_STOCHASTIC}
+
+
+def oracle_route(logits, shape, mode):
+    return orc.route(logits, shape.K, shape.M, ORC_MODE[mode], make_round_rand(shape.E, 0))
 INT_FIELDS = ("tc_counts", "counts", "expert_offsets")
 
 
@@ -58,7 +65,8 @@ def run_gpu(shape, dtype, mode, inp):
     p = moe.problem(shape.T, shape.d, shape.n, shape.E, shape.K, shape.M, dtype, mode)
     dev = torch.device("cuda", 0)
     X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
-    rt = moe.route(p, lg)
+    rr = round_rand_tensor(make_round_rand(shape.E, 0)).to(dev)
+    rt = moe.route(p, lg, round_rand=rr)
     O, H = moe.forward(p, X, W1, W2, rt)
     dX, dW1, dW2, dS = moe.backward(p, dO, X, H, W1, W2, rt)
     torch.cuda.synchronize()
@@ -105,6 +113,10 @@ SMALL_CASES = [
     ("wide_n", torch.bfloat16, "tr"), ("wide_n", torch.bfloat16, "tc"),
     ("all_experts", torch.bfloat16, "tr"), ("few_tokens", torch.bfloat16, "tr"),
     ("few_tokens", torch.float32, "tc"), ("m1", torch.bfloat16, "tr"),
+    # the other token-rounding subroutines
+    ("small", torch.bfloat16, "tr_up"), ("small", torch.bfloat16, "tr_down"),
+    ("small", torch.bfloat16, "tr_stochastic"), ("tiny", torch.float32, "tr_stochastic"),
+    ("wide_n", torch.bfloat16, "tr_up"), ("ragged", torch.bfloat16, "tr_down"),
 ]
 
 
@@ -116,7 +128,7 @@ def test_parity_full_oracle(name, dtype, mode):
     inp = make_layer_inputs(shape, dtype=dtype, seed=0)
     g = run_gpu(shape, dtype, mode, inp)
     a = np_inputs(inp)
-    ref = orc.route(a["logits"], shape.K, shape.M, orc.TR if mode == "tr" else orc.TC)
+    ref = oracle_route(a["logits"], shape, mode)
     check_routing(g, ref, shape)
     S = ref.S
     O, c = orc.forward(a["X"], a["W1"], a["W2"], ref)
@@ -143,12 +155,17 @@ def test_deterministic():
     inp = make_layer_inputs(shape, dtype=torch.bfloat16, seed=1)
     a = run_gpu(shape, torch.bfloat16, "tr", inp)
     b = run_gpu(shape, torch.bfloat16, "tr", inp)
-    for k in ("slot_token", "token_slots", "O", "dX", "dW1", "dW2", "dS"):
+    S = int(a["totals"][0])
+    assert int(b["totals"][0]) == S
+    for k in ("O", "dX", "dW1", "dW2"):
         assert torch.equal(a[k], b[k]), k
+    # slot-indexed outputs are defined on rows [0, S) only
+    for k in ("slot_token", "token_slots", "dS"):
+        assert torch.equal(a[k][:S], b[k][:S]), k
 
 
-LARGE_CASES = [("7b", "tr"), ("7b", "tc"), ("high_g", "tr"), ("high_sparsity", "tr"),
-               ("high_sparsity", "tc")]
+LARGE_CASES = [("7b", "tr"), ("7b", "tc"), ("7b", "tr_stochastic"), ("high_g", "tr"),
+               ("high_sparsity", "tr"), ("high_sparsity", "tc")]
 
 
 @pytest.mark.parametrize("name,mode", LARGE_CASES)
@@ -159,7 +176,7 @@ def test_parity_full_size_sampled(name, mode):
     inp = make_layer_inputs(shape, dtype=torch.bfloat16, seed=0)
     g = run_gpu(shape, torch.bfloat16, mode, inp)
     logits = inp["logits"].numpy()
-    ref = orc.route(logits, shape.K, shape.M, orc.TR if mode == "tr" else orc.TC)
+    ref = oracle_route(logits, shape, mode)
     check_routing(g, ref, shape)
     a = np_inputs(inp)
     rng = np.random.default_rng(123)
