@@ -12,6 +12,7 @@ sample of the same workload (a subset of the experts) on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 7b]
                        [--mode tc|tr|tr_up|tr_down|tr_stochastic] [--no-cpu-baseline]
+       python bench.py --sweep   (TC vs token rounding at 1, 2, 4, 8 tiles per expert)
 """
 from __future__ import annotations
 
@@ -35,6 +36,8 @@ from fine_grained_mixture_amd.profiling import kernel_model, read_traffic  # noq
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3    # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+KERNEL_NAMES = [f"route:{k}" for k in moe.ROUTE_KERNELS] + list(moe.FWD_KERNELS) + \
+    list(moe.BWD_KERNELS)
 
 
 def restrict_routing(rt, keep):
@@ -101,6 +104,83 @@ def cpu_baseline(sh, inp, mode, target_s=15.0):
     }
 
 
+def measure(sh, mode, steps, warmup, dev, T=None):
+    """Times `steps` route+fwd+bwd steps of layer `sh` (T tokens if given) in
+    routing mode `mode` after `warmup` untimed ones.  Returns the mean step
+    time, the mean time of every kernel (trace events on the stream), the
+    slot count S and the number of 128-row M tiles."""
+    inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0, T=T)
+    T = sh.T if T is None else T
+    X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
+    rr = round_rand_tensor(make_round_rand(sh.E, 0)).to(dev)  # stochastic rounding draws
+    p = moe.problem(T, sh.d, sh.n, sh.E, sh.K, sh.M, torch.bfloat16, mode)
+    sz = moe.sizes(p)
+    rt = moe.alloc_routing(p, dev)
+    ws_r = moe.workspace(sz.ws_route, dev)
+    ws_f = moe.workspace(sz.ws_fwd, dev)
+    ws_b = moe.workspace(sz.ws_bwd, dev)
+    O = torch.empty(T, sh.d, dtype=torch.bfloat16, device=dev)
+    H = torch.empty(sz.slot_cap, 2 * sh.n, dtype=torch.bfloat16, device=dev)
+    grads = (torch.empty_like(X), torch.empty_like(W1), torch.empty_like(W2),
+             torch.empty(sz.slot_cap, dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def mk(k):
+        # torch creates an event's handle on its first record
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    def step(ev=None):
+        e_r, e_f, e_b = ev if ev else (None, None, None)
+        moe.route(p, lg, rt=rt, ws=ws_r, stream=stream, events=e_r, round_rand=rr)
+        moe.forward(p, X, W1, W2, rt, out=(O, H), ws=ws_f, stream=stream, events=e_f)
+        moe.backward(p, dO, X, H, W1, W2, rt, out=grads, ws=ws_b, stream=stream, events=e_b)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(mk(len(moe.ROUTE_KERNELS) + 1), mk(len(moe.FWD_KERNELS) + 1),
+            mk(len(moe.BWD_KERNELS) + 1)) for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    per = np.zeros(len(KERNEL_NAMES))
+    for e_r, e_f, e_b in evs:
+        d = [a.elapsed_time(b) for group in (e_r, e_f, e_b) for a, b in zip(group, group[1:])]
+        per += np.array(d)
+    per /= steps
+    return {"ms": ms, "per_ms": per, "S": int(rt.totals[0].item()),
+            "tiles": int(rt.totals[1].item())}
+
+
+def sweep(dev, steps, warmup):
+    """Token choice against every token-rounding subroutine at average
+    tokens per expert T_e = T K / E of 1, 2, 4 and 8 M-tiles (the 7B layer's
+    width, T varied).  One JSON line per point: step time, slots S, executed
+    rows (whole 128-row tiles), padding waste, and TFLOPS counted on the
+    slots (useful) and on the executed rows."""
+    sh = SHAPES["7b"]
+    for ratio in (1, 2, 4, 8):
+        T = ratio * sh.M * sh.E // sh.K
+        for mode in ("tc", "tr", "tr_up", "tr_down", "tr_stochastic"):
+            r = measure(sh, mode, steps, warmup, dev, T=T)
+            rows = r["tiles"] * moe.TILE_M
+            per_row = 18 * sh.n * sh.d / (r["ms"] / 1e3) / 1e12
+            print(json.dumps({"tokens_per_expert_in_tiles": ratio, "T": T, "mode": mode,
+                              "ms_per_step": round(r["ms"], 4), "slots": r["S"],
+                              "executed_rows": rows,
+                              "padding_waste": round((rows - r["S"]) / rows, 4),
+                              "useful_tflops": round(r["S"] * per_row, 1),
+                              "executed_tflops": round(rows * per_row, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +189,9 @@ def main():
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
     ap.add_argument("--mode", default="tr", choices=sorted(moe.ROUTE_MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: TC vs token rounding at 1, 2, 4 and 8 "
+                         "M-tiles of tokens per expert (one JSON line per point)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (known HBM "
                          "traffic: 1 GiB read + 1 GiB written per launch), to scale the "
@@ -131,56 +214,13 @@ def main():
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
                           "launches": 5}))
         return
+    if args.sweep:
+        sweep(dev, args.steps, args.warmup)
+        return
     sh = SHAPES[args.config]
-    inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)
-    X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
-    rr = round_rand_tensor(make_round_rand(sh.E, 0)).to(dev)  # stochastic rounding draws
-    p = moe.problem(sh.T, sh.d, sh.n, sh.E, sh.K, sh.M, torch.bfloat16, args.mode)
-    sz = moe.sizes(p)
-    rt = moe.alloc_routing(p, dev)
-    ws_r = moe.workspace(sz.ws_route, dev)
-    ws_f = moe.workspace(sz.ws_fwd, dev)
-    ws_b = moe.workspace(sz.ws_bwd, dev)
-    O = torch.empty(sh.T, sh.d, dtype=torch.bfloat16, device=dev)
-    H = torch.empty(sz.slot_cap, 2 * sh.n, dtype=torch.bfloat16, device=dev)
-    grads = (torch.empty_like(X), torch.empty_like(W1), torch.empty_like(W2),
-             torch.empty(sz.slot_cap, dtype=torch.float32, device=dev))
-    stream = torch.cuda.current_stream(dev)
-
-    names = [f"route:{k}" for k in moe.ROUTE_KERNELS] + list(moe.FWD_KERNELS) + \
-        list(moe.BWD_KERNELS)
-    def mk(k):
-        # torch creates an event's handle on its first record
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
-        for e in evs:
-            e.record(stream)
-        return evs
-
-    def step(ev=None):
-        e_r, e_f, e_b = ev if ev else (None, None, None)
-        moe.route(p, lg, rt=rt, ws=ws_r, stream=stream, events=e_r, round_rand=rr)
-        moe.forward(p, X, W1, W2, rt, out=(O, H), ws=ws_f, stream=stream, events=e_f)
-        moe.backward(p, dO, X, H, W1, W2, rt, out=grads, ws=ws_b, stream=stream, events=e_b)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(mk(7), mk(4), mk(6)) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-
-    per = np.zeros(len(names))
-    for e_r, e_f, e_b in evs:
-        d = [a.elapsed_time(b) for group in (e_r, e_f, e_b) for a, b in zip(group, group[1:])]
-        per += np.array(d)
-    per /= args.steps
-    S = int(rt.totals[0].item())
+    r = measure(sh, args.mode, args.steps, args.warmup, dev)
+    ms, per, names = r["ms"], r["per_ms"], KERNEL_NAMES
+    S = r["S"]
     flops = sh.flops
     tflops = flops / (ms / 1e3) / 1e12
 
@@ -231,10 +271,14 @@ def main():
                    "T": sh.T, "d": sh.d, "n": sh.n, "E": sh.E, "K": sh.K, "M_tile": sh.M,
                    "slots": S, "parallelism": "single GPU"},
         "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        # 18 n d per slot actually routed, and per row executed (whole tiles)
+        "useful_tflops": 18 * S * sh.n * sh.d / (ms / 1e3) / 1e12,
+        "executed_tflops": 18 * r["tiles"] * moe.TILE_M * sh.n * sh.d / (ms / 1e3) / 1e12,
         "roofline": roof,
         "kernels_us": kernels,
     }
     if not args.no_cpu_baseline:
+        inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)  # the same seeded inputs
         out["cpu_baseline"] = cpu_baseline(sh, inp, args.mode)
     print(json.dumps(out))
 
