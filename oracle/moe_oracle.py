@@ -319,6 +319,39 @@ def backward_naive(dO, X, W1, W2, rt: Routing, cache):
 
 
 # --------------------------------------------------------------------------
+# Router
+# --------------------------------------------------------------------------
+
+def router_logits(X, Wr):
+    """Router scores l = X Wr^T in fp64 (Wr: [E, d], one row per expert).
+
+    The notes (method > overall framework; key design 1) route every token by
+    its router scores; the router itself is a linear map of the token.
+    """
+    return _f64(X) @ _f64(Wr).T
+
+
+def router_backward(dS, rt: Routing, X, Wr, logits):
+    """Gradients of the router from the gate-weight gradients dS.
+
+    The gate weight of a kept (token, expert) pair is s = p[t, e], the softmax
+    probability (no renormalisation), and the loss sees the router only
+    through those weights (routing decisions are piecewise constant and carry
+    no gradient).  So with g[t, e] = dS of the slot of (t, e), zero for pairs
+    not kept, the softmax Jacobian gives
+        dlogits[t] = p[t] * (g[t] - <p[t], g[t]>),
+    and the linear map gives dWr = dlogits^T X ([E, d]) and the router's share
+    of the input gradient dX_router = dlogits Wr ([T, d]).
+    """
+    p = softmax_probs(logits)
+    T, E = p.shape
+    g = np.zeros((T, E), dtype=np.float64)
+    g[rt.slot_token, rt.slot_expert] = _f64(dS)[: rt.S]
+    dlogits = p * (g - (p * g).sum(axis=1, keepdims=True))
+    return dlogits, dlogits.T @ _f64(X), dlogits @ _f64(Wr)
+
+
+# --------------------------------------------------------------------------
 # Sampled evaluation for full-size shapes (same arithmetic, restricted rows).
 # These recompute H from X and W1 themselves and convert only the rows and
 # experts they touch to fp64, so they also serve shapes whose full fp64 copy
