@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 from fine_grained_mixture_amd import moe  # noqa: E402
 from fine_grained_mixture_amd.inputs import (SHAPES, make_layer_inputs,  # noqa: E402
-                                             make_round_rand, round_rand_tensor)
+                                             make_round_rand, make_router_weight,
+                                             round_rand_tensor)
 from fine_grained_mixture_amd.profiling import kernel_model, read_traffic  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -160,6 +161,63 @@ def measure(sh, mode, steps, warmup, dev, T=None):
             "tiles": int(rt.totals[1].item())}
 
 
+def measure_router(sh, steps, warmup, dev):
+    """Router forward (logits = X Wr^T) and backward (dlogits, dX += dl Wr,
+    dWr) of layer `sh`, outside the metric's step: dS comes from one layer
+    step.  Returns the mean time of each router kernel in ms."""
+    inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)
+    X, W1, W2, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "dO"))
+    Wr = make_router_weight(sh, torch.bfloat16, seed=0).to(dev)
+    p = moe.problem(sh.T, sh.d, sh.n, sh.E, sh.K, sh.M, torch.bfloat16, "tr")
+    lg = moe.router_forward(p, X, Wr)
+    rt = moe.route(p, lg)
+    O, H = moe.forward(p, X, W1, W2, rt)
+    dX, dW1, dW2, dS = moe.backward(p, dO, X, H, W1, W2, rt)
+    ws = moe.workspace(moe.sizes(p).ws_router, dev)
+    out = (torch.empty(sh.T, sh.E, dtype=torch.float32, device=dev),
+           torch.empty(sh.E, sh.d, dtype=torch.bfloat16, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def mk(k):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    def step(ev=None):
+        ef, eb = ev if ev else (None, None)
+        moe.router_forward(p, X, Wr, out=lg, stream=stream, events=ef)
+        moe.router_backward(p, X, Wr, lg, dS, rt, dX, out=out, ws=ws, stream=stream, events=eb)
+
+    for _ in range(warmup):
+        step()
+    evs = [(mk(len(moe.ROUTER_FWD_KERNELS) + 1), mk(len(moe.ROUTER_BWD_KERNELS) + 1))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    names = list(moe.ROUTER_FWD_KERNELS) + list(moe.ROUTER_BWD_KERNELS)
+    per = np.zeros(len(names))
+    for ef, eb in evs:
+        per += np.array([a.elapsed_time(b) for g in (ef, eb) for a, b in zip(g, g[1:])])
+    return dict(zip(names, per / steps))
+
+
+def router_line(sh, per_ms):
+    """Router kernel times with the FLOPs of the two GEMM-shaped ones."""
+    out = {}
+    gemm = {"router_logits": 2 * sh.T * sh.d * sh.E, "router_dx": 2 * sh.T * sh.E * sh.d,
+            "router_dw": 2 * sh.T * sh.E * sh.d}
+    for k, t in per_ms.items():
+        out[k] = {"us": round(t * 1e3, 2)}
+        if k in gemm:
+            out[k]["tflops"] = round(gemm[k] / (t / 1e3) / 1e12, 1)
+    out["fwd_us"] = round(per_ms["router_logits"] * 1e3, 2)
+    out["bwd_us"] = round(sum(v for k, v in per_ms.items() if k != "router_logits") * 1e3, 2)
+    return out
+
+
 def sweep(dev, steps, warmup):
     """Token choice against every token-rounding subroutine at average
     tokens per expert T_e = T K / E of 1, 2, 4 and 8 M-tiles (the 7B layer's
@@ -276,6 +334,8 @@ def main():
         "executed_tflops": 18 * r["tiles"] * moe.TILE_M * sh.n * sh.d / (ms / 1e3) / 1e12,
         "roofline": roof,
         "kernels_us": kernels,
+        # outside the metric's step (its FLOPs are not in 18 T n K d)
+        "router": router_line(sh, measure_router(sh, args.steps, args.warmup, dev)),
     }
     if not args.no_cpu_baseline:
         inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)  # the same seeded inputs

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["moe_api.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "aggregate.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "gemm_fwd.hip", "gemm_bwd.hip", "aggregate.hip",
+           "router.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -278,6 +278,20 @@ __device__ __forceinline__ void zero_rows(char* tile, int valid) {
     *reinterpret_cast<uint4*>(tile + o) = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Zeroes the rows past the last valid row in the final, partial slab of
+// a varlen-K contraction (those rows were read from the last valid row).
+template <class Cfg, int ACOLS, int BCOLS>
+struct VarlenTail {
+  int nslabs, valid;
+  __device__ __forceinline__ void operator()(int s, char* stage) const {
+    if (s != nslabs - 1 || valid == Cfg::BK) return;
+    zero_rows<Cfg, ACOLS>(stage, valid);
+    zero_rows<Cfg, BCOLS>(stage + Cfg::A_BYTES, valid);
+    wait_lgkm0();
+    barrier();
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Fragment reads
 // ---------------------------------------------------------------------------

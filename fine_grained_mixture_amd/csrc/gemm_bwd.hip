@@ -338,19 +338,6 @@ __device__ __forceinline__ void store_tile(const Accum<Cfg>& acc, char* lds,
   store_acc_staged(acc, lds, [&](int r) -> T* { return out + int64_t(r) * ld; });
 }
 
-// Zeroes the rows past the expert's last slot in the final, partial slab of
-// a varlen-K contraction (those rows were read from the last valid slot).
-template <class Cfg, int ACOLS, int BCOLS>
-struct VarlenTail {
-  int nslabs, valid;
-  __device__ __forceinline__ void operator()(int s, char* stage) const {
-    if (s != nslabs - 1 || valid == Cfg::BK) return;
-    zero_rows<Cfg, ACOLS>(stage, valid);
-    zero_rows<Cfg, BCOLS>(stage + Cfg::A_BYTES, valid);
-    wait_lgkm0();
-    barrier();
-  }
-};
 
 // dW1_e[i][j] = sum over the expert's slots k of X[tok_k][i] * dH[k][j]:
 // both operands MN-major, rows = slots (X rows gathered through slot_token).

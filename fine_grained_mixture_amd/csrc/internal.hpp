@@ -67,4 +67,25 @@ hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* d
 hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2, void* vws,
                       hipStream_t st);
 
+// Router (linear scores l = X Wr^T and their backward from dS).
+struct RouterDims {
+  int Ep;            // E rounded up to 128: row length of the padded dl copy
+  int kc, nchunks;   // tokens per dWr partial, number of partials
+  size_t dlp_bytes;  // padded dl copy in the operand type
+  size_t ws_bytes;   // + fp32 partials of dWr
+};
+RouterDims router_dims(int T, int d, int E, bool f32);
+hipError_t launch_router_fwd(bool f32, const void* X, const void* Wr, float* logits, int T,
+                             int d, int E, hipStream_t st);
+struct RouterBwdArgs {
+  int T, d, E;
+  bool f32;
+  const void *X, *Wr;
+  const float *logits, *dS;
+  const int32_t *token_offsets, *token_slots, *expert_offsets;
+  float* dlogits;
+  void *dWr, *dX, *ws;
+};
+hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t st, const TraceHook& tr);
+
 }  // namespace moe

@@ -55,6 +55,7 @@ void sizes_of(const moe_problem* p, moe_sizes_t* s) {
   // fp32 partial sums) reuses once dX has been aggregated
   const size_t vw = moe::varlen_ws_bytes(p->dtype == MOE_F32, int(p->d), int(p->n), int(p->E),
                                          s->slot_cap);
+  s->ws_router = moe::router_dims(int(p->T), int(p->d), int(p->E), p->dtype == MOE_F32).ws_bytes;
   s->ws_bwd = align256(size_t(s->slot_cap * 2 * p->n * es)) +
               align256(size_t(s->slot_cap * p->n * es)) +
               std::max(align256(size_t(s->slot_cap * p->d * es)), vw);
@@ -239,6 +240,52 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
   e = moe::launch_dw2(a, As, dO, dW2, dXt, sm);
   tr.mark(sm, 5);
   return hip_status(e);
+}
+
+int moe_router_fwd(const moe_problem* p, const void* X, const void* Wr, float* logits,
+                   void* stream, const moe_trace* trace) {
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(X) || !aligned16(Wr) || !aligned16(logits) || !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  hipStream_t sm = static_cast<hipStream_t>(stream);
+  const moe::TraceHook tr = hook(trace);
+  tr.mark(sm, 0);
+  const hipError_t e = moe::launch_router_fwd(p->dtype == MOE_F32, X, Wr, logits, int(p->T),
+                                              int(p->d), int(p->E), sm);
+  tr.mark(sm, 1);
+  return hip_status(e);
+}
+
+int moe_router_bwd(const moe_problem* p, const void* X, const void* Wr, const float* logits,
+                   const float* dS, const moe_routing* r, float* dlogits, void* dWr, void* dX,
+                   void* ws, size_t ws_bytes, void* stream, const moe_trace* trace) {
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(X) || !aligned16(Wr) || !aligned16(logits) || !aligned16(dS) ||
+      !routing_ok(r) || !aligned16(dlogits) || !aligned16(dWr) || !aligned16(dX) ||
+      !aligned16(ws) || !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  moe_sizes_t s;
+  sizes_of(p, &s);
+  if (ws_bytes < s.ws_router) return MOE_ERR_WORKSPACE;
+  moe::RouterBwdArgs a;
+  a.T = int(p->T);
+  a.d = int(p->d);
+  a.E = int(p->E);
+  a.f32 = p->dtype == MOE_F32;
+  a.X = X;
+  a.Wr = Wr;
+  a.logits = logits;
+  a.dS = dS;
+  a.token_offsets = r->token_offsets;
+  a.token_slots = r->token_slots;
+  a.expert_offsets = r->expert_offsets;
+  a.dlogits = dlogits;
+  a.dWr = dWr;
+  a.dX = dX;
+  a.ws = ws;
+  return hip_status(moe::launch_router_bwd(a, static_cast<hipStream_t>(stream), hook(trace)));
 }
 
 }  // extern "C"

@@ -119,3 +119,16 @@ def make_round_rand(E: int, seed: int = 0) -> np.ndarray:
 def round_rand_tensor(rand: np.ndarray) -> torch.Tensor:
     """[E] int32 CPU tensor holding the bits of the uint32 draws."""
     return torch.from_numpy(np.ascontiguousarray(rand.astype(np.uint32).view(np.int32)))
+
+
+def make_router_weight(shape: LayerShape | str, dtype=torch.bfloat16, seed=0) -> torch.Tensor:
+    """Router weights Wr [E, d] (one row per expert) from their own PCG64
+    stream seeded with (seed, 0x40D7): N(0, 1/d) (std 1/sqrt(fan_in)), or
+    N(0, 0.02^2) for the tiny layer; rounded to `dtype` like the other
+    weights.  The layer inputs above are unaffected."""
+    if isinstance(shape, str):
+        shape = SHAPES[shape]
+    rng = np.random.default_rng([seed, 0x40D7])
+    scale = 0.02 if shape.init == "tiny" else 1 / np.sqrt(shape.d)
+    Wr = rng.standard_normal((shape.E, shape.d), dtype=np.float32) * np.float32(scale)
+    return _cast(Wr, dtype)

@@ -26,6 +26,8 @@ TILE_M = 128
 ROUTE_KERNELS = ("route_topk", "route_count", "route_scan", "route_select", "route_tcount",
                  "route_tslots")
 FWD_KERNELS = ("up_swiglu", "down", "aggregate_O")
+ROUTER_FWD_KERNELS = ("router_logits",)
+ROUTER_BWD_KERNELS = ("router_dlogits", "router_dx", "router_dw", "router_dw_reduce")
 BWD_KERNELS = ("dh", "dxt", "aggregate_dX", "dw1", "dw2")
 
 
@@ -38,7 +40,7 @@ class Problem(ctypes.Structure):
 class Sizes(ctypes.Structure):
     _fields_ = [("slot_cap", ctypes.c_int64), ("tile_cap", ctypes.c_int64),
                 ("ws_route", ctypes.c_size_t), ("ws_fwd", ctypes.c_size_t),
-                ("ws_bwd", ctypes.c_size_t)]
+                ("ws_bwd", ctypes.c_size_t), ("ws_router", ctypes.c_size_t)]
 
 
 ROUTING_FIELDS = ("tc_counts", "counts", "expert_offsets", "expert_order", "topk_ids",
@@ -76,9 +78,13 @@ def lib():
     L.moe_fwd.argtypes = [P(Problem), V, V, V, P(RoutingStruct), V, V, V, S, V, P(Trace)]
     L.moe_bwd.argtypes = [P(Problem), V, V, V, V, V, P(RoutingStruct), V, V, V, V, V, S, V,
                           P(Trace)]
+    L.moe_router_fwd.argtypes = [P(Problem), V, V, V, V, P(Trace)]
+    L.moe_router_bwd.argtypes = [P(Problem), V, V, V, V, P(RoutingStruct), V, V, V, V, S, V,
+                                 P(Trace)]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
-    for f in ("moe_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_abi_version"):
+    for f in ("moe_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_router_fwd", "moe_router_bwd",
+              "moe_abi_version"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -241,6 +247,43 @@ def backward(p: Problem, dO, X, H, W1, W2, rt: Routing, out=None, ws=None, strea
     return dX, dW1, dW2, dS
 
 
+
+def router_forward(p: Problem, X, Wr, out=None, stream=None, events=None) -> torch.Tensor:
+    """moe_router_fwd: logits = X Wr^T in fp32, [T, E]."""
+    dt = torch_dtype(p)
+    lg = out if out is not None else torch.empty(p.T, p.E, dtype=torch.float32, device=X.device)
+    tr = _trace(events)
+    _check(lib().moe_router_fwd(ctypes.byref(p), _dev(X, "X", dt, (p.T, p.d)),
+                                _dev(Wr, "Wr", dt, (p.E, p.d)),
+                                _dev(lg, "logits", torch.float32, (p.T, p.E)), _stream(stream),
+                                ctypes.byref(tr) if tr else None))
+    return lg
+
+
+def router_backward(p: Problem, X, Wr, logits, dS, rt: Routing, dX, out=None, ws=None,
+                    stream=None, events=None):
+    """moe_router_bwd: returns dlogits [T, E] fp32 and dWr [E, d]; adds the
+    router's share of the input gradient to dX in place."""
+    dt = torch_dtype(p)
+    s = sizes(p)
+    dev = X.device
+    dl, dWr = out if out is not None else (
+        torch.empty(p.T, p.E, dtype=torch.float32, device=dev),
+        torch.empty(p.E, p.d, dtype=dt, device=dev))
+    ws = ws if ws is not None else workspace(s.ws_router, dev)
+    tr = _trace(events)
+    _check(lib().moe_router_bwd(ctypes.byref(p), _dev(X, "X", dt, (p.T, p.d)),
+                                _dev(Wr, "Wr", dt, (p.E, p.d)),
+                                _dev(logits, "logits", torch.float32, (p.T, p.E)),
+                                _dev(dS, "dS", torch.float32, (s.slot_cap,)),
+                                ctypes.byref(rt.struct),
+                                _dev(dl, "dlogits", torch.float32, (p.T, p.E)),
+                                _dev(dWr, "dWr", dt, (p.E, p.d)), _dev(dX, "dX", dt, (p.T, p.d)),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
+                                ctypes.byref(tr) if tr else None))
+    return dl, dWr
+
+
 class MoELayerFunction(torch.autograd.Function):
     """Autograd wrapper.  Saves exactly X and H (plus the routing metadata) for
     the backward; the router-facing gradient dS is left on the routing object
@@ -268,3 +311,34 @@ class MoELayerFunction(torch.autograd.Function):
 
 def moe_layer(X, W1, W2, logits, K, M_tile, mode="tr"):
     return MoELayerFunction.apply(X, W1, W2, logits, K, M_tile, mode)
+
+
+class MoERouterLayerFunction(torch.autograd.Function):
+    """The whole layer with its router: logits = X Wr^T are computed by the
+    library, and the backward returns dX (experts' and router's shares), dWr,
+    dW1 and dW2.  Saves X, H, Wr, W1, W2, the logits and the routing; the
+    draws of stochastic rounding (``round_rand``) are an input."""
+
+    @staticmethod
+    def forward(ctx, X, Wr, W1, W2, K, M_tile, mode, round_rand):
+        T, d = X.shape
+        E, _, n2 = W1.shape
+        p = problem(T, d, n2 // 2, E, K, M_tile, X.dtype, mode)
+        logits = router_forward(p, X, Wr)
+        rt = route(p, logits, round_rand=round_rand)
+        O, H = forward(p, X, W1, W2, rt)
+        ctx.save_for_backward(X, H, Wr, W1, W2, logits)
+        ctx.moe = (p, rt)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        X, H, Wr, W1, W2, logits = ctx.saved_tensors
+        p, rt = ctx.moe
+        dX, dW1, dW2, dS = backward(p, dO.contiguous(), X, H, W1, W2, rt)
+        _, dWr = router_backward(p, X, Wr, logits, dS, rt, dX)
+        return dX, dWr, dW1, dW2, None, None, None, None
+
+
+def moe_router_layer(X, Wr, W1, W2, K, M_tile, mode="tr", round_rand=None):
+    return MoERouterLayerFunction.apply(X, Wr, W1, W2, K, M_tile, mode, round_rand)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Rows per M tile of the grouped GEMMs; the tile schedule in moe_routing is
  * expressed in these units. */
@@ -85,6 +85,7 @@ typedef struct {
   size_t ws_route;  /* workspace bytes moe_route needs                         */
   size_t ws_fwd;    /* workspace bytes moe_fwd needs                           */
   size_t ws_bwd;    /* workspace bytes moe_bwd needs                           */
+  size_t ws_router; /* workspace bytes moe_router_bwd needs                    */
 } moe_sizes_t;
 
 /*
@@ -114,7 +115,9 @@ typedef struct {
  * records trace->events[i] (hipEvent_t, created by the caller) on `stream`
  * before its i-th kernel and trace->events[kernels] after the last one.
  * moe_route launches 6 kernels, moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
- * dX aggregate, dW1, dW2).  NULL disables tracing.
+ * dX aggregate, dW1, dW2; the dW segments include the chunk plan and the
+ * reduction of split experts), moe_router_fwd 1, moe_router_bwd 4 (dlogits,
+ * router dX, dWr partials, dWr reduction).  NULL disables tracing.
  */
 typedef struct {
   void **events;
@@ -189,6 +192,38 @@ int moe_bwd(const moe_problem *p, const void *dO, const void *X, const void *H,
             const void *W1, const void *W2, const moe_routing *r, void *dX,
             void *dW1, void *dW2, float *dS, void *ws, size_t ws_bytes,
             void *stream, const moe_trace *trace);
+
+/*
+ * Router forward (notes, method > overall framework and key design 1: tokens
+ * are routed by their router scores).  Reading: the router is a linear map
+ * with one row per expert.
+ *   logits[t, e] = sum_i X[t, i] Wr[e, i]   fp32 result, fp32 accumulation
+ * X: [T, d] and Wr: [E, d] in p->dtype; logits: [T, E] fp32 (what moe_route
+ * reads).  All device buffers, caller-owned, 16-byte aligned; asynchronous
+ * on `stream`.  Errors as moe_sizes, MOE_ERR_INVALID for null or misaligned
+ * buffers.
+ */
+int moe_router_fwd(const moe_problem *p, const void *X, const void *Wr, float *logits,
+                   void *stream, const moe_trace *trace);
+
+/*
+ * Router backward (notes, method > overall framework: the layer's backward
+ * yields the router gradients; dS is what moe_bwd hands to the router).  The
+ * gate weight of a kept pair is s = softmax(logits[t])[e], so with g[t, e] =
+ * dS of the slot of (t, e) (0 where the pair is not kept; routing decisions
+ * carry no gradient):
+ *   dlogits[t] = p[t] * (g[t] - <p[t], g[t]>),  p = softmax(logits[t]) (fp32)
+ *   dWr        = dlogits^T X                    [E, d], p->dtype
+ *   dX        += dlogits Wr                     [T, d], p->dtype, in place:
+ *                the router's share of the input gradient is added to the
+ *                experts' share that moe_bwd wrote
+ * Inputs: X, Wr as in moe_router_fwd; logits [T, E] fp32; dS [slot_cap] fp32
+ * from moe_bwd; `r` from moe_route.  Outputs: dlogits [T, E] fp32, dWr, dX.
+ * ws: at least sizes.ws_router bytes.
+ */
+int moe_router_bwd(const moe_problem *p, const void *X, const void *Wr, const float *logits,
+                   const float *dS, const moe_routing *r, float *dlogits, void *dWr, void *dX,
+                   void *ws, size_t ws_bytes, void *stream, const moe_trace *trace);
 
 /* Static, NUL-terminated description of a moe_status value. */
 const char *moe_status_string(int status);

@@ -28,12 +28,12 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert names == ["moe_abi_version", "moe_bwd", "moe_fwd", "moe_route", "moe_sizes",
-                     "moe_status_string"]
+    assert names == ["moe_abi_version", "moe_bwd", "moe_fwd", "moe_route", "moe_router_bwd",
+                     "moe_router_fwd", "moe_sizes", "moe_status_string"]
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -138,3 +138,20 @@ def test_null_trace_event_rejected():
     tr = moe.Trace(ev, 7)
     assert L.moe_route(ctypes.byref(p), FAKE, None, ctypes.byref(_routing()), FAKE, need, None,
                        ctypes.byref(tr)) == INVALID
+
+
+def test_router_validation_before_launch():
+    L = moe.lib()
+    p = moe.problem(256, 128, 64, 8, 2, 16)
+    s = moe.sizes(p)
+    assert s.ws_router > 0
+    assert L.moe_router_fwd(ctypes.byref(p), None, FAKE, FAKE, None, None) == INVALID
+    assert L.moe_router_fwd(ctypes.byref(p), FAKE, FAKE, FAKE + 4, None, None) == INVALID
+    rr = ctypes.byref(_routing())
+    args = [FAKE] * 4
+    assert L.moe_router_bwd(ctypes.byref(p), *args, rr, FAKE, FAKE, FAKE, FAKE,
+                            s.ws_router - 1, None, None) == WORKSPACE
+    assert L.moe_router_bwd(ctypes.byref(p), *args, ctypes.byref(_routing(0)), FAKE, FAKE,
+                            FAKE, FAKE, s.ws_router, None, None) == INVALID
+    assert L.moe_router_bwd(ctypes.byref(p), *args, rr, None, FAKE, FAKE, FAKE, s.ws_router,
+                            None, None) == INVALID
