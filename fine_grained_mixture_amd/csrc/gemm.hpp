@@ -495,6 +495,29 @@ struct RowStage {
   __device__ __forceinline__ void put(int row, int col, const T (&v)[4]) const {
     __builtin_memcpy(buf + row * LDR + col * int(sizeof(T)), v, sizeof(v));
   }
+  __device__ __forceinline__ void get(int row, int col, T (&v)[4]) const {
+    __builtin_memcpy(v, buf + row * LDR + col * int(sizeof(T)), sizeof(v));
+  }
+  // The inverse of flush: whole rows from global memory into the buffer
+  // (rowptr(r) == nullptr leaves row r as it is).
+  template <class RowPtr>
+  __device__ __forceinline__ void fill(RowPtr rowptr) const {
+    constexpr int CPR = RB / 16;
+    const int lane = threadIdx.x & 63;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int idx = lane; idx < 32 * CPR; idx += 64) {
+      const int r = idx / CPR, c = idx % CPR;
+      const T* g = rowptr(r);
+      if (g) {
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(g) + c * 16);
+        char* dst = buf + r * LDR + c * 16;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(v.z, v.w);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
   // rowptr(r): destination of staged column 0 of block row r, or nullptr.
   template <class RowPtr>
   __device__ __forceinline__ void flush(RowPtr rowptr) const {

@@ -24,8 +24,13 @@
 namespace moe {
 namespace {
 
+// dX and dWr: two stages (64 KB of LDS), so two workgroups share a CU; the
+// dX contraction is only Ep deep and the dWr chunks a few slabs each
 template <class T>
-using RouterCfg = TileCfg<T, 128, 128, 2, 2, 3, 128>;
+using RouterCfg = TileCfg<T, 128, 128, 2, 2, 2, 128>;
+// logits: 64-token tiles, so that a 16k-token batch fills every CU
+template <class T>
+using LogitsCfg = TileCfg<T, 64, 128, 1, 4, 3, 128>;
 
 // l[t, e] = sum_i X[t, i] Wr[e, i]: A = X rows, B = Wr rows (both K-major).
 // Rows of Wr past E lie past the end of its buffer and read as zeros.
@@ -158,22 +163,31 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_router_dx(
   Accum<Cfg> acc;
   acc.init();
   pipeline<Cfg, true, false>(acc, lds, Ep / Cfg::BK, la, lb, NoTail{});
+  // Read-modify-write of dX through the per-wave staging buffer: whole rows
+  // in, each lane adds its accumulators to its four columns, whole rows out.
+  using St = RowStage<T, Cfg::WTN>;
+  static_assert(St::BYTES * Cfg::NW <= Cfg::LDS_BYTES, "staging fits");
+  const St stg{lds + wave_id() * St::BYTES};
+  const int r32 = acc.lane & 31, h = acc.lane >> 5;
+  const int cw = j0 + Cfg::colblock(acc.wn, 0);
 #pragma unroll
   for (int a = 0; a < Cfg::MB; ++a) {
-    const int t = t0 + acc.row(a);
-    if (t >= Tn) continue;
+    const int rb = t0 + acc.wm * Cfg::WTM + a * 32;
+    auto rows = [&](int r) -> T* { return rb + r < Tn ? dX + int64_t(rb + r) * d + cw : nullptr; };
+    stg.fill(rows);
 #pragma unroll
     for (int b = 0; b < Cfg::NB; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        T* px = dX + int64_t(t) * d + j0 + acc.col(b, q);
+        const int col = b * 32 + q * 8 + h * 4;
         T v[4];
-        __builtin_memcpy(v, px, sizeof(v));
+        stg.get(r32, col, v);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           v[c] = Elem<T>::store(Elem<T>::load(v[c]) + acc.acc[a][b][q * 4 + c]);
-        __builtin_memcpy(px, v, sizeof(v));
+        stg.put(r32, col, v);
       }
+    stg.flush(rows);
   }
 }
 
@@ -215,17 +229,29 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_router_dw(
       }
 }
 
-// dWr[e, i] = sum over chunks (in order) of the partials, rows e < E.
+// dWr[e, i] = sum over chunks (in order) of the partials, rows e < E; four
+// consecutive elements per thread, four chunks' loads in flight at a time.
 template <class T>
 __global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ partials,
                                                        T* __restrict__ dWr, int E, int Ep, int d,
                                                        int nchunks) {
-  const int64_t n = int64_t(E) * d, stride = int64_t(Ep) * d;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += int64_t(gridDim.x) * 256) {
-    float s = 0.0f;
-    for (int c = 0; c < nchunks; ++c) s += partials[c * stride + i];
-    dWr[i] = Elem<T>::store(s);
+  const int64_t n4 = int64_t(E) * d / 4, stride = int64_t(Ep) * d;
+  for (int64_t i4 = int64_t(blockIdx.x) * 256 + threadIdx.x; i4 < n4;
+       i4 += int64_t(gridDim.x) * 256) {
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < nchunks; c0 += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = c0 + u < nchunks ? reinterpret_cast<const float4*>(partials + (c0 + u) * stride)[i4]
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // chunk order
+        s[0] += v[u].x; s[1] += v[u].y; s[2] += v[u].z; s[3] += v[u].w;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dWr[4 * i4 + c] = Elem<T>::store(s[c]);
   }
 }
 
@@ -249,7 +275,7 @@ RouterDims router_dims(int Tn, int d, int E, bool f32) {
 template <class T>
 hipError_t router_fwd_t(const void* X, const void* Wr, float* logits, int Tn, int d, int E,
                         hipStream_t st) {
-  using Cfg = RouterCfg<T>;
+  using Cfg = LogitsCfg<T>;
   const int grid = ((Tn + Cfg::BM - 1) / Cfg::BM) * ((E + Cfg::BN - 1) / Cfg::BN);
   hipLaunchKernelGGL((k_router_logits<Cfg>), dim3(grid), dim3(Cfg::kThreads), 0, st,
                      static_cast<const T*>(X), static_cast<const T*>(Wr), logits, Tn, d, E);
@@ -282,8 +308,8 @@ hipError_t router_bwd_t(const RouterBwdArgs& a, hipStream_t st, const TraceHook&
                      dim3(r.nchunks * (r.Ep / Cfg::BM) * (a.d / Cfg::BN)), dim3(Cfg::kThreads),
                      0, st, dlp, static_cast<const T*>(a.X), partials, a.T, a.d, r.Ep, r.kc);
   tr.mark(st, 3);
-  const int64_t n = int64_t(a.E) * a.d;
-  hipLaunchKernelGGL((k_router_reduce<T>), dim3(unsigned(std::min<int64_t>((n + 255) / 256, 4096))),
+  const int64_t n4 = int64_t(a.E) * a.d / 4;  // d is a multiple of 128
+  hipLaunchKernelGGL((k_router_reduce<T>), dim3(unsigned(std::min<int64_t>((n4 + 255) / 256, 4096))),
                      dim3(256), 0, st, partials, static_cast<T*>(a.dWr), a.E, r.Ep, a.d,
                      r.nchunks);
   tr.mark(st, 4);
