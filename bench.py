@@ -239,6 +239,33 @@ def sweep(dev, steps, warmup):
                               "executed_tflops": round(rows * per_row, 1)}), flush=True)
 
 
+def granularity_sweep(dev, steps, warmup):
+    """Iso-FLOP sweep over granularity G = d/n at d = 1024, T = 16384 and
+    sparsity K/E = 1/16, with nK = 1024 fixed (so 18 T n K d is the same at
+    every point): G = 2, 4, 8, 16 -> (n, K, E) = (512, 2, 32), (256, 4, 64),
+    (128, 8, 128), (64, 16, 256); token rounding.  One JSON line per point:
+    step time, TFLOPS, the forward arithmetic intensity, and the bytes kept
+    for the backward by this layer (X, H) against a backward that caches
+    every intermediate (plus gathered X, A, Y)."""
+    from fine_grained_mixture_amd.inputs import LayerShape
+    from fine_grained_mixture_amd.profiling import activation_bytes, arithmetic_intensity
+
+    T, d = 16384, 1024
+    for G in (2, 4, 8, 16):
+        n = d // G
+        K = 1024 // n
+        E = 16 * K
+        sh = LayerShape(f"g{G}", T, d, n, E, K, 128, "fan_in", "normal_bias")
+        r = measure(sh, "tr", steps, warmup, dev)
+        mem = activation_bytes(T, d, n, K, r["S"])
+        print(json.dumps({"G": G, "n": n, "K": K, "E": E, "T": T, "d": d,
+                          "ms_per_step": round(r["ms"], 4),
+                          "tflops": round(sh.flops / (r["ms"] / 1e3) / 1e12, 1),
+                          "arithmetic_intensity": round(arithmetic_intensity(T, d, n, K, E), 1),
+                          "saved_bytes_minimal": mem["minimal"],
+                          "saved_bytes_caching": mem["caching"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +274,9 @@ def main():
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
     ap.add_argument("--mode", default="tr", choices=sorted(moe.ROUTE_MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--granularity", action="store_true",
+                    help="instead of the benchmark line: iso-FLOP sweep over d/n = 2, 4, 8, 16 "
+                         "(one JSON line per point)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: TC vs token rounding at 1, 2, 4 and 8 "
                          "M-tiles of tokens per expert (one JSON line per point)")
@@ -274,6 +304,9 @@ def main():
         return
     if args.sweep:
         sweep(dev, args.steps, args.warmup)
+        return
+    if args.granularity:
+        granularity_sweep(dev, args.steps, args.warmup)
         return
     sh = SHAPES[args.config]
     r = measure(sh, args.mode, args.steps, args.warmup, dev)

@@ -80,29 +80,6 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
     const float s = slot_weight[srow];
     const T* hrow = H + int64_t(srow) * n2;
     float part = 0.0f;
-    T out[3][Cfg::NB][4][4];  // dH gate, dH up, s * A
-#pragma unroll
-    for (int b = 0; b < Cfg::NB; ++b) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = acc.col(b, q);
-        T g4[4], u4[4];
-        __builtin_memcpy(g4, hrow + j, sizeof(g4));
-        __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float x = acc.acc[a][b][q * 4 + c];  // dA'
-          const float g = Elem<T>::load(g4[c]), u = Elem<T>::load(u4[c]);
-          const float sg = sigmoidf_(g), silu = g * sg;
-          const float av = silu * u;
-          part += x * av;
-          const float da = s * x;
-          out[0][b][q][c] = Elem<T>::store(da * u * sg * (1.0f + g * (1.0f - sg)));
-          out[1][b][q][c] = Elem<T>::store(da * silu);
-          out[2][b][q][c] = Elem<T>::store(s * av);
-        }
-      }
-    }
     const int rb = row0 + acc.wm * Cfg::WTM + a * 32;
     auto flush = [&](int o) {
       T* base = o == 0 ? dH + cw : o == 1 ? dH + n + cw : As + cw;
@@ -110,17 +87,60 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
       stg[o].flush(
           [&](int r) -> T* { return rb + r < rend ? base + int64_t(rb + r) * ld : nullptr; });
     };
+    // output o of the four values at column group (b, q): 0 = dH gate,
+    // 1 = dH up, 2 = s * A; o == 0 also accumulates the dS row sum
+    auto outputs = [&](int o, int b, int q, T (&v)[4]) {
+      const int j = acc.col(b, q);
+      T g4[4], u4[4];
+      __builtin_memcpy(g4, hrow + j, sizeof(g4));
+      __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
 #pragma unroll
-    for (int o = 0; o < 3; ++o) {
+      for (int c = 0; c < 4; ++c) {
+        const float x = acc.acc[a][b][q * 4 + c];  // dA'
+        const float g = Elem<T>::load(g4[c]), u = Elem<T>::load(u4[c]);
+        const float sg = sigmoidf_(g), silu = g * sg;
+        const float av = silu * u;
+        const float da = s * x;
+        if (o == 0) {
+          part += x * av;
+          v[c] = Elem<T>::store(da * u * sg * (1.0f + g * (1.0f - sg)));
+        } else if (o == 1) {
+          v[c] = Elem<T>::store(da * silu);
+        } else {
+          v[c] = Elem<T>::store(s * av);
+        }
+      }
+    };
+    if constexpr (kAll) {
+      // three buffers: every value computed once, all three staged together
 #pragma unroll
       for (int b = 0; b < Cfg::NB; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) stg[o].put(r32, b * 32 + q * 8 + h * 4, out[o][b][q]);
-      if constexpr (!kAll) flush(o);
-    }
-    if constexpr (kAll) {
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int o = 0; o < 3; ++o) {
+            T v[4];
+            outputs(o, b, q, v);
+            stg[o].put(r32, b * 32 + q * 8 + h * 4, v);
+          }
 #pragma unroll
       for (int o = 0; o < 3; ++o) flush(o);
+    } else {
+      // one buffer: one output at a time (the small H fragment is reread and
+      // the activation recomputed, which keeps the registers in check)
+#pragma unroll
+      for (int o = 0; o < 3; ++o) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the three passes apart in the schedule
+#pragma unroll
+        for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            T v[4];
+            outputs(o, b, q, v);
+            stg[o].put(r32, b * 32 + q * 8 + h * 4, v);
+          }
+        flush(o);
+      }
     }
     part += __shfl_xor(part, 32, 64);
     if (acc.lane < 32) red[acc.wn * BM + i] = part;
@@ -430,6 +450,10 @@ hipError_t dh_t(const LayerArgs& a, const void* dO, const void* W2, const void* 
       else dh_launch<TileCfg<T, 128, 256, 2, 2, 3>>(a, dO, W2, H, dH, As, dS, st);
       break;
     case 384: dh_launch<TileCfg<T, 64, 384, 1, 4, 3>>(a, dO, W2, H, dH, As, dS, st); break;
+    case 512:
+      if constexpr (sizeof(T) == 2) dh_launch<DhWide512>(a, dO, W2, H, dH, As, dS, st);
+      else dh_launch<TileCfg<T, 64, 512, 1, 4, 2>>(a, dO, W2, H, dH, As, dS, st);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -29,7 +29,8 @@ int check_problem(const moe_problem* p) {
   if (p->mode < MOE_ROUTE_TC || p->mode > MOE_ROUTE_TR_STOCHASTIC) return MOE_ERR_INVALID;
   if (p->K > 32 || p->E > 1024 || p->M_tile > 1024) return MOE_ERR_UNSUPPORTED;
   if (p->d % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (p->n != 64 && p->n != 128 && p->n != 256 && p->n != 384) return MOE_ERR_UNSUPPORTED;
+  if (p->n != 64 && p->n != 128 && p->n != 256 && p->n != 384 && p->n != 512)
+    return MOE_ERR_UNSUPPORTED;
   // Kernels index rows with 32-bit element offsets, and the GEMM operand
   // loads address each array through a buffer descriptor with a 32-bit byte
   // extent.

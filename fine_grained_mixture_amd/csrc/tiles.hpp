@@ -45,6 +45,7 @@ using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
 using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 #endif
 
+using DhWide512 = TileCfg<bf16_t, 64, 512, 1, 4, 2, 128>;  // dH for n = 512 (one wave per SIMD)
 using UpMid = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128, true>;
 using UpNarrow = TileCfg<bf16_t, 128, 128, 2, 2, 3, 128, true>;
 using RowsMid = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;

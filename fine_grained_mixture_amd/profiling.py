@@ -62,6 +62,25 @@ def kernel_model(name, sh, S, esz=2):
     return m.get(name)
 
 
+def arithmetic_intensity(T, d, n, K, E):
+    """Forward arithmetic intensity (FLOP per byte) of a fine-grained MoE
+    layer as the notes state it (background and motivation, with G = d/n and
+    rho = K/E), in the dimensionally consistent reading
+    3 / ((2 + 2G)/d + 3/(T rho)): a byte count of the forward (X_e read, W1,
+    A written and read, W2, Y written; the H write-back left out)."""
+    G, rho = d / n, K / E
+    return 3.0 / ((2.0 + 2.0 * G) / d + 3.0 / (T * rho))
+
+
+def activation_bytes(T, d, n, K, S, esz=2):
+    """Bytes kept from the forward for the backward.  minimal: X and H (S
+    rows of 2n) in the operand type (notes, key design 3: 2Td + 4TKn at S =
+    TK for bf16).  caching: what a backward that keeps every intermediate
+    holds besides: the gathered X_e, A and Y (S rows of d, n and d)."""
+    minimal = esz * (T * d + S * 2 * n)
+    return {"minimal": minimal, "caching": minimal + esz * (S * d + S * n + S * d)}
+
+
 def kernel_sources_sha256(root=ROOT):
     """sha256 over the kernel sources (csrc/*.hip, *.hpp) and include/*.h."""
     files = sorted(glob.glob(os.path.join(root, "fine_grained_mixture_amd", "csrc", "*.hip")) +

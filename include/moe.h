@@ -127,7 +127,7 @@ typedef struct {
 /* Host only; touches no device.  Validates `p` and fills `out`.
  * Errors: MOE_ERR_INVALID for null arguments or T, d, n, E, K, M_tile < 1,
  * K > E, unknown dtype/mode; MOE_ERR_UNSUPPORTED for K > 32, E > 1024,
- * d % 128 != 0, n not in {64, 128, 256, 384}, M_tile > 1024, sizes whose
+ * d % 128 != 0, n not in {64, 128, 256, 384, 512}, M_tile > 1024, sizes whose
  * slot or element counts overflow 32-bit indexing, or an X / dO / H / dH /
  * A / Y array (T x d, slot_cap x 2n, slot_cap x d) of more than 4 GiB - 1
  * bytes. */

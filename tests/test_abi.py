@@ -63,7 +63,7 @@ def test_sizes_fp32_doubles_transients():
 @pytest.mark.parametrize("field,value,status", [
     ("T", 0, INVALID), ("d", -128, INVALID), ("K", 9, INVALID), ("M_tile", 0, INVALID),
     ("dtype", 5, INVALID), ("mode", 5, INVALID), ("mode", -1, INVALID), ("K", 33, UNSUPPORTED),
-    ("d", 192, UNSUPPORTED), ("n", 96, UNSUPPORTED), ("n", 512, UNSUPPORTED),
+    ("d", 192, UNSUPPORTED), ("n", 96, UNSUPPORTED), ("n", 640, UNSUPPORTED),
     ("E", 2048, UNSUPPORTED), ("M_tile", 4096, UNSUPPORTED), ("T", 1 << 26, UNSUPPORTED),
 ])
 def test_invalid_problems(field, value, status):

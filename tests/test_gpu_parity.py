@@ -35,6 +35,8 @@ EXTRA = {
     "few_tokens": LayerShape("few_tokens", 20, 128, 64, 8, 1, 16, "tiny", "router"),
     # M_tile = 1: token rounding is token choice
     "m1": LayerShape("m1", 512, 256, 64, 16, 2, 1, "fan_in", "iid"),
+    # n = 512 (granularity d/n = 2 at d = 1024): the 64 x 512 dH tile
+    "n512": LayerShape("n512", 1024, 1024, 512, 16, 2, 64, "fan_in", "normal_bias"),
 }
 TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
 ORC_MODE = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
@@ -117,6 +119,7 @@ SMALL_CASES = [
     ("small", torch.bfloat16, "tr_up"), ("small", torch.bfloat16, "tr_down"),
     ("small", torch.bfloat16, "tr_stochastic"), ("tiny", torch.float32, "tr_stochastic"),
     ("wide_n", torch.bfloat16, "tr_up"), ("ragged", torch.bfloat16, "tr_down"),
+    ("n512", torch.bfloat16, "tr"), ("n512", torch.float32, "tc"),
 ]
 
 

@@ -29,3 +29,14 @@ def test_kernel_model_flops_sum_to_layer_flops():
                for k in ("up_swiglu", "down", "dh", "dxt", "dw1", "dw2"))
     assert gemm == 18 * S * sh.n * sh.d == sh.flops
     assert profiling.kernel_model("route_topk", sh, S) is None
+
+
+def test_intensity_and_saved_bytes_agree_with_the_oracle():
+    # the benchmark's helpers and the oracle's are written independently
+    from oracle import moe_oracle as orc
+    for T, d, n, K, E in [(16384, 1536, 256, 8, 128), (16384, 1024, 512, 2, 32),
+                          (8192, 2048, 384, 8, 512)]:
+        assert abs(profiling.arithmetic_intensity(T, d, n, K, E)
+                   - orc.arithmetic_intensity(T, d, n, K, E)) < 1e-9
+        assert profiling.activation_bytes(T, d, n, K, T * K)["minimal"] == \
+            orc.cached_activation_bytes(T, d, K, n)
