@@ -266,6 +266,53 @@ def granularity_sweep(dev, steps, warmup):
                           "saved_bytes_caching": mem["caching"]}), flush=True)
 
 
+def vendor_gemms(dev, steps, warmup, config):
+    """hipBLASLt (torch.mm / torch.bmm, bf16, contiguous operands) at the
+    GEMM shapes of one layer step with S = T K slots, as dense GEMMs without
+    gather or fused epilogue (bmm: one batch per expert of S / E rows).  A
+    reference point for the grouped kernels, not part of the path.  One JSON
+    line per shape."""
+    sh = SHAPES[config]
+    S, d, n, E = sh.T * sh.K, sh.d, sh.n, sh.E
+    Se = S // E
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=bf, generator=g)
+
+    cases = [
+        ("up mm [S,d]x[d,2n]", (rnd(S, d), rnd(d, 2 * n)), torch.mm, 2 * S * d * 2 * n),
+        ("down mm [S,n]x[n,d]", (rnd(S, n), rnd(n, d)), torch.mm, 2 * S * n * d),
+        ("dxt mm [S,2n]x[2n,d]", (rnd(S, 2 * n), rnd(2 * n, d)), torch.mm, 2 * S * 2 * n * d),
+        ("dA' mm [S,d]x[d,n]", (rnd(S, d), rnd(d, n)), torch.mm, 2 * S * d * n),
+        ("up bmm E x [S/E,d]x[d,2n]", (rnd(E, Se, d), rnd(E, d, 2 * n)), torch.bmm,
+         2 * S * d * 2 * n),
+        ("down bmm E x [S/E,n]x[n,d]", (rnd(E, Se, n), rnd(E, n, d)), torch.bmm, 2 * S * n * d),
+        ("dxt bmm E x [S/E,2n]x[2n,d]", (rnd(E, Se, 2 * n), rnd(E, 2 * n, d)), torch.bmm,
+         2 * S * 2 * n * d),
+        ("dW1 bmm E x [d,S/E]x[S/E,2n]", (rnd(E, d, Se), rnd(E, Se, 2 * n)), torch.bmm,
+         2 * S * d * 2 * n),
+        ("dW2 bmm E x [n,S/E]x[S/E,d]", (rnd(E, n, Se), rnd(E, Se, d)), torch.bmm,
+         2 * S * n * d),
+    ]
+    for name, (a, b), fn, fl in cases:
+        for _ in range(warmup):
+            fn(a, b)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            fn(a, b)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        print(json.dumps({"gemm": name, "config": config, "us": round(ms * 1e3, 1),
+                          "tflops": round(fl / (ms / 1e3) / 1e12, 1)}), flush=True)
+        del a, b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +327,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: TC vs token rounding at 1, 2, 4 and 8 "
                          "M-tiles of tokens per expert (one JSON line per point)")
+    ap.add_argument("--vendor-gemms", action="store_true",
+                    help="instead of the benchmark line: hipBLASLt (torch.mm / bmm) at the "
+                         "layer's GEMM shapes, dense and contiguous, as a reference point")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (known HBM "
                          "traffic: 1 GiB read + 1 GiB written per launch), to scale the "
@@ -307,6 +357,9 @@ def main():
         return
     if args.granularity:
         granularity_sweep(dev, args.steps, args.warmup)
+        return
+    if args.vendor_gemms:
+        vendor_gemms(dev, args.steps, args.warmup, args.config)
         return
     sh = SHAPES[args.config]
     r = measure(sh, args.mode, args.steps, args.warmup, dev)

@@ -37,6 +37,14 @@ EXTRA = {
     "m1": LayerShape("m1", 512, 256, 64, 16, 2, 1, "fan_in", "iid"),
     # n = 512 (granularity d/n = 2 at d = 1024): the 64 x 512 dH tile
     "n512": LayerShape("n512", 1024, 1024, 512, 16, 2, 64, "fan_in", "normal_bias"),
+    # a single token
+    "one_token": LayerShape("one_token", 1, 128, 64, 4, 2, 16, "fan_in", "iid"),
+    # one expert holding every token (E = K = 1: a dense SwiGLU MLP)
+    "one_expert": LayerShape("one_expert", 200, 256, 128, 1, 1, 32, "fan_in", "iid"),
+    # an M_tile that is not a power of two
+    "tile48": LayerShape("tile48", 900, 256, 128, 12, 3, 48, "fan_in", "normal_bias"),
+    # the largest expert count (E = 1024), few tokens per expert
+    "e1024": LayerShape("e1024", 512, 128, 64, 1024, 4, 16, "fan_in", "zipf_bias"),
 }
 TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
 ORC_MODE = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
@@ -120,6 +128,11 @@ SMALL_CASES = [
     ("small", torch.bfloat16, "tr_stochastic"), ("tiny", torch.float32, "tr_stochastic"),
     ("wide_n", torch.bfloat16, "tr_up"), ("ragged", torch.bfloat16, "tr_down"),
     ("n512", torch.bfloat16, "tr"), ("n512", torch.float32, "tc"),
+    # edge shapes
+    ("one_token", torch.bfloat16, "tr"), ("one_token", torch.float32, "tc"),
+    ("one_expert", torch.bfloat16, "tr"), ("one_expert", torch.bfloat16, "tc"),
+    ("tile48", torch.bfloat16, "tr"), ("tile48", torch.bfloat16, "tr_stochastic"),
+    ("e1024", torch.bfloat16, "tr"), ("e1024", torch.bfloat16, "tc"),
 ]
 
 
