@@ -54,6 +54,30 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
 
   Accum<Cfg> acc;
   acc.init();
+  // The H values of this lane's accumulator positions (and the gate weights)
+  // do not depend on the product: when they fit in 64 registers they are
+  // loaded before the main loop, so their latency hides behind it instead of
+  // stalling the epilogue.
+  constexpr bool kPreH = Cfg::NW == 8 && Cfg::MB * Cfg::NB * 4 * 2 * 4 * int(sizeof(T)) <= 256;
+  T hpre[kPreH ? Cfg::MB : 1][kPreH ? Cfg::NB : 1][4][2][4];
+  float spre[kPreH ? Cfg::MB : 1];
+  if constexpr (kPreH) {
+#pragma unroll
+    for (int a = 0; a < Cfg::MB; ++a) {
+      const int slot = row0 + acc.row(a);
+      const int srow = slot < rend ? slot : row0;
+      const T* hrow = H + int64_t(srow) * n2;
+      spre[a] = slot_weight[srow];
+#pragma unroll
+      for (int b = 0; b < Cfg::NB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = acc.col(b, q);
+          __builtin_memcpy(hpre[a][b][q][0], hrow + j, 4 * sizeof(T));
+          __builtin_memcpy(hpre[a][b][q][1], hrow + n + j, 4 * sizeof(T));
+        }
+    }
+  }
   pipeline<Cfg, true, true>(acc, lds, d / Cfg::BK, la, lb, NoTail{});
 
   // Epilogue: per row, dS = <dA', A> (A from the stored H), dH = dSwiGLU and
@@ -77,7 +101,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
     const int i = acc.row(a), slot = row0 + i;
     const bool live = slot < rend;
     const int srow = live ? slot : row0;  // rows past the expert read a valid row
-    const float s = slot_weight[srow];
+    float s;
+    if constexpr (kPreH) s = spre[a];
+    else s = slot_weight[srow];
     const T* hrow = H + int64_t(srow) * n2;
     float part = 0.0f;
     const int rb = row0 + acc.wm * Cfg::WTM + a * 32;
@@ -92,8 +118,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
     auto outputs = [&](int o, int b, int q, T (&v)[4]) {
       const int j = acc.col(b, q);
       T g4[4], u4[4];
-      __builtin_memcpy(g4, hrow + j, sizeof(g4));
-      __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
+      if constexpr (kPreH) {
+        __builtin_memcpy(g4, hpre[a][b][q][0], sizeof(g4));
+        __builtin_memcpy(u4, hpre[a][b][q][1], sizeof(u4));
+      } else {
+        __builtin_memcpy(g4, hrow + j, sizeof(g4));
+        __builtin_memcpy(u4, hrow + n + j, sizeof(u4));
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float x = acc.acc[a][b][q * 4 + c];  // dA'
