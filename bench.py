@@ -142,16 +142,23 @@ def measure(sh, mode, steps, warmup, dev, T=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(mk(len(moe.ROUTE_KERNELS) + 1), mk(len(moe.FWD_KERNELS) + 1),
-            mk(len(moe.BWD_KERNELS) + 1)) for _ in range(steps)]
+    # The step time comes from steps without trace events (an event record
+    # costs GPU time of its own: about 3 us each, 50 us per step); the
+    # per-kernel times come from the same number of traced steps right after.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
-        step(evs[i])
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
+    evs = [(mk(len(moe.ROUTE_KERNELS) + 1), mk(len(moe.FWD_KERNELS) + 1),
+            mk(len(moe.BWD_KERNELS) + 1)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     per = np.zeros(len(KERNEL_NAMES))
     for e_r, e_f, e_b in evs:
         d = [a.elapsed_time(b) for group in (e_r, e_f, e_b) for a, b in zip(group, group[1:])]

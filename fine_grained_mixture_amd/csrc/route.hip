@@ -16,9 +16,10 @@
 //                 token-choice bitmap (expert-major); clears the token-major
 //                 bitmap rows of its tokens
 //   route_count   per expert: f_e = popcount of its bitmap row, r_e
-//   route_scan    one workgroup: expert offsets, tile schedule, expert order
 //   route_select  per expert: token-rounding threshold (radix select on the
-//                 64-bit keys), slot list in token order, gate weights
+//                 64-bit keys), slot list in token order, gate weights; one
+//                 extra workgroup scans the counts: expert offsets, the
+//                 M-tile schedule, the expert order by count, the totals
 //   route_tcount  per block of tokens: number of slots
 //   route_tslots  per token: CSR offset and its slots in ascending expert order
 #include "moe.h"
@@ -176,6 +177,23 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
   for (int e = tid; e < E; e += kTopkThreads) bits_e[int64_t(e) * nw + blockIdx.x] = sbits[e];
 }
 
+// The rounded count r_e of an expert with f token-choice tokens: the nearest
+// multiple of M (ties down), always up, always down, or up with probability
+// (f mod M) / M against the expert's 32-bit draw; a count is only rounded up
+// when that many distinct tokens exist (hi <= T).
+__device__ __forceinline__ int rounded_count(int f, int T, int M, int mode,
+                                             const uint32_t* __restrict__ round_rand, int e) {
+  if (mode == MOE_ROUTE_TC) return f;
+  const int lo = (f / M) * M;
+  const int hi = (f % M == 0) ? f : lo + M;
+  bool up;
+  if (mode == MOE_ROUTE_TR) up = (hi - f) < (f - lo);
+  else if (mode == MOE_ROUTE_TR_UP) up = hi > f;
+  else if (mode == MOE_ROUTE_TR_DOWN) up = false;
+  else up = uint64_t(round_rand[e]) * uint64_t(M) < (uint64_t(f - lo) << 32);
+  return (up && hi <= T) ? hi : lo;
+}
+
 // Per expert: f_e = number of set bits in its row of the token-choice bitmap,
 // and the rounded count r_e.
 __global__ __launch_bounds__(256) void route_count(
@@ -190,32 +208,20 @@ __global__ __launch_bounds__(256) void route_count(
   int f;
   block_excl_scan(c, sh, &f);
   if (threadIdx.x == 0) {
-    int r = f;
-    if (mode != MOE_ROUTE_TC) {
-      const int lo = (f / M) * M;
-      const int hi = (f % M == 0) ? f : lo + M;
-      bool up;
-      if (mode == MOE_ROUTE_TR) up = (hi - f) < (f - lo);
-      else if (mode == MOE_ROUTE_TR_UP) up = hi > f;
-      else if (mode == MOE_ROUTE_TR_DOWN) up = false;
-      else up = uint64_t(round_rand[e]) * uint64_t(M) < (uint64_t(f - lo) << 32);
-      r = (up && hi <= T) ? hi : lo;
-    }
     tc_counts[e] = f;
-    counts[e] = r;
+    counts[e] = rounded_count(f, T, M, mode, round_rand, e);
   }
 }
 
 // One workgroup of 1024 threads, one expert per thread (E <= 1024): slot
 // offsets, the M-tile schedule and the experts ordered by descending count.
-__global__ __launch_bounds__(kScanThreads) void route_scan(
-    const int32_t* __restrict__ counts, int E, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ expert_order, int32_t* __restrict__ tile_expert,
-    int32_t* __restrict__ tile_row, int32_t* __restrict__ totals) {
-  __shared__ int sh[kScanThreads / 64 + 1];
-  __shared__ int sr[1024];
+__device__ __forceinline__ void scan_body(int r, int E, int* sh, int* sr,
+                                          int32_t* __restrict__ expert_offsets,
+                                          int32_t* __restrict__ expert_order,
+                                          int32_t* __restrict__ tile_expert,
+                                          int32_t* __restrict__ tile_row,
+                                          int32_t* __restrict__ totals) {
   const int e = threadIdx.x;
-  const int r = e < E ? counts[e] : 0;
   sr[e] = r;
   int S, ntiles;
   const int off = block_excl_scan(r, sh, &S);
@@ -228,10 +234,16 @@ __global__ __launch_bounds__(kScanThreads) void route_scan(
       tile_row[tbase + i] = off + i * kTileM;
     }
     // rank among experts by descending count, ties to the lower expert
+    // (four counts per LDS read; entries past E hold 0 and sit above e, so
+    // they never count)
     int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const int rj = sr[j];
-      rank += (rj > r) || (rj == r && j < e);
+#pragma unroll 4
+    for (int j = 0; j < E; j += 4) {
+      const int4 q = *reinterpret_cast<const int4*>(sr + j);
+      rank += (q.x > r) || (q.x == r && j < e);
+      rank += (q.y > r) || (q.y == r && j + 1 < e);
+      rank += (q.z > r) || (q.z == r && j + 2 < e);
+      rank += (q.w > r) || (q.w == r && j + 3 < e);
     }
     expert_order[rank] = e;
   }
@@ -241,6 +253,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan(
     totals[1] = ntiles;
   }
 }
+
 
 // Per expert: keep the r_e best tokens under the key (is-TC, p) descending,
 // equal keys to the lower token, then list them in token order as slots.
@@ -256,7 +269,9 @@ constexpr int kSelFinish = 256;
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void route_select(
     int T, int E, const int32_t* __restrict__ tc_counts,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ expert_offsets,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ expert_order, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ tile_row, int32_t* __restrict__ totals,
     const uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e,
     uint32_t* __restrict__ bits_t, int32_t* __restrict__ wbase,
     int32_t* __restrict__ slot_token, float* __restrict__ slot_weight) {
@@ -269,7 +284,21 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
   __shared__ uint64_t cand[kSelFinish];  // keys left under the prefix (early finish)
   __shared__ int s_ncand;
   __shared__ uint64_t s_thr;
+  __shared__ __attribute__((aligned(16))) int sr[1024];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  if (e == E) {
+    // the extra workgroup: offsets, tile schedule, expert order and totals
+    scan_body(tid < E ? counts[tid] : 0, E, sh, sr, expert_offsets, expert_order, tile_expert,
+              tile_row, totals);
+    return;
+  }
+  // this expert's first slot: the counts of the experts before it
+  int off;
+  {
+    int before;
+    block_excl_scan(tid < e ? counts[tid] : 0, sh, &before);
+    off = before;
+  }
   const int f = tc_counts[e], r = counts[e];
   const int nw = (T + 31) >> 5;
   const int W = (E + 31) >> 5;
@@ -427,7 +456,6 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
 
   // Compaction in token order: the word pass lists the kept tokens; a flat
   // pass over the expert's slots then fetches all gate weights in parallel.
-  const int off = expert_offsets[e];
   int carry = 0;
   for (int base = 0; base < nw; base += kSelThreads) {
     const int w = base + tid;
@@ -541,32 +569,22 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
   hipLaunchKernelGGL(route_count, dim3(E), dim3(256), 0, st, T, a.M, a.mode, a.round_rand, bits_e,
                      a.tc_counts, a.counts);
   tr.mark(st, 2);
-  hipLaunchKernelGGL(route_scan, dim3(1), dim3(kScanThreads), 0, st, a.counts, E,
-                     a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row, a.totals);
+#define MOE_SELECT(N)                                                                        \
+  hipLaunchKernelGGL(route_select<N>, dim3(E + 1), dim3(kSelThreads), 0, st, T, E, a.tc_counts, \
+                     a.counts, a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row,    \
+                     a.totals, keys, bits_e, bits_t, wbase, a.slot_token, a.slot_weight)
+  if (T <= 8 * kSelThreads) MOE_SELECT(8);
+  else if (T <= 16 * kSelThreads) MOE_SELECT(16);
+  else if (T <= 32 * kSelThreads) MOE_SELECT(32);
+  else MOE_SELECT(0);
+#undef MOE_SELECT
   tr.mark(st, 3);
-  if (T <= 8 * kSelThreads)
-    hipLaunchKernelGGL(route_select<8>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
-                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
-                       a.slot_weight);
-  else if (T <= 16 * kSelThreads)
-    hipLaunchKernelGGL(route_select<16>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
-                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
-                       a.slot_weight);
-  else if (T <= 32 * kSelThreads)
-    hipLaunchKernelGGL(route_select<32>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
-                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
-                       a.slot_weight);
-  else
-    hipLaunchKernelGGL(route_select<0>, dim3(E), dim3(kSelThreads), 0, st, T, E, a.tc_counts,
-                       a.counts, a.expert_offsets, keys, bits_e, bits_t, wbase, a.slot_token,
-                       a.slot_weight);
-  tr.mark(st, 4);
   const dim3 tgrid(cdiv(T, 256));
   hipLaunchKernelGGL(route_tcount, tgrid, dim3(256), 0, st, T, E, bits_t, block_sum);
-  tr.mark(st, 5);
+  tr.mark(st, 4);
   hipLaunchKernelGGL(route_tslots, tgrid, dim3(256), 0, st, T, E, bits_t, bits_e, wbase,
                      a.expert_offsets, block_sum, a.token_offsets, a.token_slots);
-  tr.mark(st, 6);
+  tr.mark(st, 5);
   return hipGetLastError();
 }
 

@@ -45,6 +45,9 @@ EXTRA = {
     "tile48": LayerShape("tile48", 900, 256, 128, 12, 3, 48, "fan_in", "normal_bias"),
     # the largest expert count (E = 1024), few tokens per expert
     "e1024": LayerShape("e1024", 512, 128, 64, 1024, 4, 16, "fan_in", "zipf_bias"),
+    # E = 1024 with many tokens: the select grid's extra scan workgroup and
+    # every expert's own offset sum run over the full 1024 counts
+    "big_bitmap": LayerShape("big_bitmap", 8192, 128, 64, 1024, 4, 16, "fan_in", "iid"),
 }
 TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
 ORC_MODE = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
@@ -133,6 +136,7 @@ SMALL_CASES = [
     ("one_expert", torch.bfloat16, "tr"), ("one_expert", torch.bfloat16, "tc"),
     ("tile48", torch.bfloat16, "tr"), ("tile48", torch.bfloat16, "tr_stochastic"),
     ("e1024", torch.bfloat16, "tr"), ("e1024", torch.bfloat16, "tc"),
+    ("big_bitmap", torch.bfloat16, "tr"),
 ]
 
 
