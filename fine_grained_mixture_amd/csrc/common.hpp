@@ -156,7 +156,7 @@ struct RouteWs {
   size_t bits_e;   // uint32 [E][nw] selection bitmap, expert-major (nw = ceil(T/32))
   size_t bits_t;   // uint32 [T][W]  selection bitmap, token-major (W = ceil(E/32))
   size_t wbase;    // int32  [E][nw] slots of expert e in words before w
-  size_t block_sum;  // int32 [ceil(T/256)] slots per block of 256 tokens
+  size_t block_sum;  // int32 [E][ceil(T/256)] slots of expert e per block of 256 tokens
   size_t total;
   __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
   __host__ __device__ static RouteWs make(int64_t T, int64_t E) {
@@ -167,7 +167,7 @@ struct RouteWs {
     w.bits_e = o; o = align(o + size_t(E) * nw * 4);
     w.bits_t = o; o = align(o + size_t(T) * W * 4);
     w.wbase = o;  o = align(o + size_t(E) * nw * 4);
-    w.block_sum = o; o = align(o + size_t((T + 255) / 256) * 4);
+    w.block_sum = o; o = align(o + size_t(E) * ((T + 255) / 256) * 4);
     w.total = o;
     return w;
   }

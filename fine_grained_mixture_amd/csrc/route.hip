@@ -17,10 +17,10 @@
 //                 bitmap rows of its tokens
 //   route_count   per expert: f_e = popcount of its bitmap row, r_e
 //   route_select  per expert: token-rounding threshold (radix select on the
-//                 64-bit keys), slot list in token order, gate weights; one
+//                 64-bit keys), slot list in token order, gate weights, and
+//                 the expert's slots added to per-256-token block counts; one
 //                 extra workgroup scans the counts: expert offsets, the
 //                 M-tile schedule, the expert order by count, the totals
-//   route_tcount  per block of tokens: number of slots
 //   route_tslots  per token: CSR offset and its slots in ascending expert order
 #include "moe.h"
 #include "common.hpp"
@@ -274,7 +274,8 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
     int32_t* __restrict__ tile_row, int32_t* __restrict__ totals,
     const uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e,
     uint32_t* __restrict__ bits_t, int32_t* __restrict__ wbase,
-    int32_t* __restrict__ slot_token, float* __restrict__ slot_weight) {
+    int32_t* __restrict__ slot_token, float* __restrict__ slot_weight,
+    int32_t* __restrict__ block_sum) {
   // 16 copies of the 256-bin histogram; the +1 pad puts the copies of one
   // digit in 16 different banks
   __shared__ uint32_t hist[16][257];
@@ -462,6 +463,7 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
     const uint32_t word = (w < nw) ? be[w] : 0u;
     int chunk;
     const int ex = block_excl_scan(__popc(word), sh, &chunk);
+    int written = 0;
     if (w < nw) {
       const int wb = carry + ex;
       wbase[int64_t(e) * nw + w] = wb;
@@ -473,7 +475,13 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
         m &= m - 1;
         slot_token[off + wb + i++] = w * 32 + b;
       }
+      written = i;
     }
+    // this expert's slots in each block of 256 tokens (8 words, 8
+    // consecutive lanes), for the token CSR
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) written += __shfl_xor(written, o, 64);
+    if ((lane & 7) == 0 && w < nw) block_sum[int64_t(e) * ((nw + 7) >> 3) + (w >> 3)] = written;
     carry += chunk;
   }
   __syncthreads();
@@ -487,52 +495,72 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
   }
 }
 
-// Per block of 256 tokens: the number of slots of those tokens.
-__global__ __launch_bounds__(256) void route_tcount(int T, int E,
-                                                    const uint32_t* __restrict__ bits_t,
-                                                    int32_t* __restrict__ block_sum) {
-  __shared__ int sh[256 / 64 + 1];
-  const int W = (E + 31) >> 5, t = blockIdx.x * 256 + threadIdx.x;
-  int c = 0;
-  if (t < T)
-    for (int w = 0; w < W; ++w) c += __popc(bits_t[int64_t(t) * W + w]);
-  int total;
-  block_excl_scan(c, sh, &total);
-  if (threadIdx.x == 0) block_sum[blockIdx.x] = total;
-}
-
-// Per token: CSR offset (earlier blocks' sums + exclusive scan inside the
-// block) and the token's slots in ascending expert order.
+// Per token: CSR offset (earlier blocks' slots, summed over the experts'
+// per-block counts, + exclusive scan inside the block) and the token's slots
+// in ascending expert order.
 __global__ __launch_bounds__(256) void route_tslots(
     int T, int E, const uint32_t* __restrict__ bits_t, const uint32_t* __restrict__ bits_e,
     const int32_t* __restrict__ wbase, const int32_t* __restrict__ expert_offsets,
     const int32_t* __restrict__ block_sum, int32_t* __restrict__ token_offsets,
     int32_t* __restrict__ token_slots) {
+  // LDS: expert offsets [E]; wbase and bits_e of this block's 8 token words
+  // [E][8] each; the block's rows of the token-major bitmap [256][W]
+  extern __shared__ int32_t dyn[];
+  int32_t* s_off = dyn;
+  int32_t* s_wb = s_off + E;
+  uint32_t* s_be = reinterpret_cast<uint32_t*>(s_wb + E * 8);
+  uint32_t* s_bt = s_be + E * 8;
   __shared__ int sh[256 / 64 + 1];
-  const int W = (E + 31) >> 5, nw = (T + 31) >> 5;
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int W = (E + 31) >> 5, nw = (T + 31) >> 5, nblk = (nw + 7) >> 3;
+  const int tid = threadIdx.x, t0 = blockIdx.x * 256, t = t0 + tid, tw0 = blockIdx.x * 8;
+  // stage the lookups of this block's tokens (coalesced), so that the slot
+  // loop below reads LDS only
+  for (int i = tid; i < E; i += 256) s_off[i] = expert_offsets[i];
+  for (int i = tid; i < E * 8; i += 256) {
+    const int e = i >> 3, tw = tw0 + (i & 7);
+    s_wb[i] = tw < nw ? wbase[int64_t(e) * nw + tw] : 0;
+    s_be[i] = tw < nw ? bits_e[int64_t(e) * nw + tw] : 0u;
+  }
+  const int nrow = min(256, T - t0);
+  for (int i = tid; i < nrow * W; i += 256) s_bt[i] = bits_t[int64_t(t0) * W + i];
+  // slots of all earlier blocks: the entries [e][b] with b < this block, read
+  // in batches of 8 per thread through a buffer descriptor (positions past
+  // the count get an offset past the end and read 0, so no load waits behind
+  // a branch)
+  const int nb = blockIdx.x, n = E * nb;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(block_sum), 0, E * nblk * 4, 0x00020000);
   int before = 0;
-  for (int b = threadIdx.x; b < int(blockIdx.x); b += 256) before += block_sum[b];
+  for (int i0 = 0; i0 < n; i0 += 256 * 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      const uint32_t off = i < n ? uint32_t((i / nb) * nblk + i % nb) * 4u : 0xfffffff0u;
+      v[u] = int(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) before += v[u];
+  }
   int base;
-  block_excl_scan(before, sh, &base);  // base = sum over all earlier blocks
+  block_excl_scan(before, sh, &base);  // base = sum over all earlier blocks (syncs the LDS)
   int c = 0;
   if (t < T)
-    for (int w = 0; w < W; ++w) c += __popc(bits_t[int64_t(t) * W + w]);
+    for (int w = 0; w < W; ++w) c += __popc(s_bt[tid * W + w]);
   int total;
   const int j0 = base + block_excl_scan(c, sh, &total);
   if (t < T) token_offsets[t] = j0;
   if (t == T - 1) token_offsets[T] = j0 + c;
   if (t >= T) return;
-  const int tw = t >> 5;
+  const int k = tid >> 5;  // this token's word among the block's 8
   const uint32_t below = (1u << (t & 31)) - 1u;
   int j = j0;
   for (int w = 0; w < W; ++w) {
-    uint32_t m = bits_t[int64_t(t) * W + w];
+    uint32_t m = s_bt[tid * W + w];
     while (m) {
       const int e = w * 32 + __ffs(m) - 1;
       m &= m - 1;
-      const int64_t q = int64_t(e) * nw + tw;
-      token_slots[j++] = expert_offsets[e] + wbase[q] + __popc(bits_e[q] & below);
+      token_slots[j++] = s_off[e] + s_wb[e * 8 + k] + __popc(s_be[e * 8 + k] & below);
     }
   }
 }
@@ -572,19 +600,18 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
 #define MOE_SELECT(N)                                                                        \
   hipLaunchKernelGGL(route_select<N>, dim3(E + 1), dim3(kSelThreads), 0, st, T, E, a.tc_counts, \
                      a.counts, a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row,    \
-                     a.totals, keys, bits_e, bits_t, wbase, a.slot_token, a.slot_weight)
+                     a.totals, keys, bits_e, bits_t, wbase, a.slot_token, a.slot_weight,     \
+                     block_sum)
   if (T <= 8 * kSelThreads) MOE_SELECT(8);
   else if (T <= 16 * kSelThreads) MOE_SELECT(16);
   else if (T <= 32 * kSelThreads) MOE_SELECT(32);
   else MOE_SELECT(0);
 #undef MOE_SELECT
   tr.mark(st, 3);
-  const dim3 tgrid(cdiv(T, 256));
-  hipLaunchKernelGGL(route_tcount, tgrid, dim3(256), 0, st, T, E, bits_t, block_sum);
+  const size_t tslots_lds = size_t(E) * 4 + size_t(E) * 8 * 4 * 2 + size_t(256) * cdiv(E, 32) * 4;
+  hipLaunchKernelGGL(route_tslots, dim3(cdiv(T, 256)), dim3(256), tslots_lds, st, T, E, bits_t,
+                     bits_e, wbase, a.expert_offsets, block_sum, a.token_offsets, a.token_slots);
   tr.mark(st, 4);
-  hipLaunchKernelGGL(route_tslots, tgrid, dim3(256), 0, st, T, E, bits_t, bits_e, wbase,
-                     a.expert_offsets, block_sum, a.token_offsets, a.token_slots);
-  tr.mark(st, 5);
   return hipGetLastError();
 }
 

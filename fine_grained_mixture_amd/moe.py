@@ -23,7 +23,7 @@ ROUTE_MODES = {"tc": MOE_ROUTE_TC, "tr": MOE_ROUTE_TR, "tr_up": MOE_ROUTE_TR_UP,
                "tr_down": MOE_ROUTE_TR_DOWN, "tr_stochastic": MOE_ROUTE_TR_STOCHASTIC}
 TILE_M = 128
 
-ROUTE_KERNELS = ("route_topk", "route_count", "route_select", "route_tcount", "route_tslots")
+ROUTE_KERNELS = ("route_topk", "route_count", "route_select", "route_tslots")
 FWD_KERNELS = ("up_swiglu", "down", "aggregate_O")
 ROUTER_FWD_KERNELS = ("router_logits",)
 ROUTER_BWD_KERNELS = ("router_dlogits", "router_dx", "router_dw", "router_dw_reduce")

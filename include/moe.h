@@ -114,8 +114,8 @@ typedef struct {
  * at least the number of kernels the call launches plus one, the call
  * records trace->events[i] (hipEvent_t, created by the caller) on `stream`
  * before its i-th kernel and trace->events[kernels] after the last one.
- * moe_route launches 5 kernels (top-K, counts, select with the offset scan,
- * token counts, token slots), moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
+ * moe_route launches 4 kernels (top-K, counts, select with the offset scan,
+ * token CSR), moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
  * dX aggregate, dW1, dW2; the dW segments include the chunk plan and the
  * reduction of split experts), moe_router_fwd 1, moe_router_bwd 4 (dlogits,
  * router dX, dWr partials, dWr reduction).  NULL disables tracing.
