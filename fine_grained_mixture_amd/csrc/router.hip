@@ -67,42 +67,48 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_router_logits(
   }
 }
 
-// One wave per token; lane l holds experts e = l + 64 j.  The slot ids of the
-// token come from the token CSR; the expert of a slot is found by binary
-// search in the expert offsets (staged in LDS).
+// One wave per token; lane l holds experts e = l + 64 j, j < EPL = Ep / 64.
+// The slot ids of the token come from the token CSR; the expert of a slot is
+// found by binary search in the expert offsets (staged in LDS).  The logits
+// are read through a buffer descriptor (positions past E read 0 and are
+// masked), so all EPL loads of a lane are in flight together.
 constexpr int kDlThreads = 256;
-constexpr int kDlMaxEPL = 16;  // E <= 1024
 
-template <class T>
+template <class T, int EPL>
 __global__ __launch_bounds__(kDlThreads) void k_router_dlogits(
     const float* __restrict__ logits, const float* __restrict__ dS,
     const int32_t* __restrict__ token_offsets, const int32_t* __restrict__ token_slots,
     const int32_t* __restrict__ expert_offsets, float* __restrict__ dlogits,
     T* __restrict__ dlp, int Tn, int E, int Ep) {
   __shared__ int off[1025];
-  __shared__ float g[kDlThreads / 64][1024];
+  __shared__ float g[kDlThreads / 64][64 * EPL];
   for (int i = threadIdx.x; i <= E; i += kDlThreads) off[i] = expert_offsets[i];
-  __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * (kDlThreads / 64) + w;
-  if (t >= Tn) return;
-  const float* lrow = logits + int64_t(t) * E;
-  float x[kDlMaxEPL], p[kDlMaxEPL];
+  const bool valid = t < Tn;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(logits + int64_t(valid ? t : 0) * E), 0, E * 4, 0x00020000);
+  float x[EPL], p[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(e) * 4u, 0, 0));
+    g[w][e] = 0.0f;
+  }
+  __syncthreads();  // off[] staged (g is per wave)
+  if (!valid) return;
   float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kDlMaxEPL; ++j) {
-    const int e = lane + 64 * j;
-    x[j] = e < E ? lrow[e] : -INFINITY;
+  for (int j = 0; j < EPL; ++j) {
+    if (lane + 64 * j >= E) x[j] = -INFINITY;
     m = fmaxf(m, x[j]);
-    g[w][e < E ? e : 0] = 0.0f;  // lanes past E rewrite entry 0 with 0
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   float z = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kDlMaxEPL; ++j) {
-    const int e = lane + 64 * j;
-    p[j] = e < E ? __expf(x[j] - m) : 0.0f;
+  for (int j = 0; j < EPL; ++j) {
+    p[j] = lane + 64 * j < E ? __expf(x[j] - m) : 0.0f;
     z += p[j];
   }
 #pragma unroll
@@ -123,23 +129,18 @@ __global__ __launch_bounds__(kDlThreads) void k_router_dlogits(
   asm volatile("" ::: "memory");
   float dot = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kDlMaxEPL; ++j) {
-    const int e = lane + 64 * j;
+  for (int j = 0; j < EPL; ++j) {
     p[j] *= rz;
-    if (e < E) dot += p[j] * g[w][e];
+    dot += p[j] * g[w][lane + 64 * j];  // p = 0 past E
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
 #pragma unroll
-  for (int j = 0; j < kDlMaxEPL; ++j) {
+  for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) {
-      const float v = p[j] * (g[w][e] - dot);
-      dlogits[int64_t(t) * E + e] = v;
-      dlp[int64_t(t) * Ep + e] = Elem<T>::store(v);
-    } else if (e < Ep) {
-      dlp[int64_t(t) * Ep + e] = Elem<T>::store(0.0f);
-    }
+    const float v = e < E ? p[j] * (g[w][e] - dot) : 0.0f;  // rows padded with zeros to Ep
+    if (e < E) dlogits[int64_t(t) * E + e] = v;
+    dlp[int64_t(t) * Ep + e] = Elem<T>::store(v);
   }
 }
 
@@ -296,9 +297,21 @@ hipError_t router_bwd_t(const RouterBwdArgs& a, hipStream_t st, const TraceHook&
   T* dlp = reinterpret_cast<T*>(w);
   float* partials = reinterpret_cast<float*>(w + r.dlp_bytes);
   tr.mark(st, 0);
-  hipLaunchKernelGGL((k_router_dlogits<T>), dim3((a.T + 3) / 4), dim3(kDlThreads), 0, st,
-                     a.logits, a.dS, a.token_offsets, a.token_slots, a.expert_offsets,
-                     a.dlogits, dlp, a.T, a.E, r.Ep);
+#define MOE_DLOGITS(EPL)                                                                    \
+  hipLaunchKernelGGL((k_router_dlogits<T, EPL>), dim3((a.T + 3) / 4), dim3(kDlThreads), 0, st, \
+                     a.logits, a.dS, a.token_offsets, a.token_slots, a.expert_offsets,        \
+                     a.dlogits, dlp, a.T, a.E, r.Ep)
+  switch (r.Ep / 64) {  // Ep is a multiple of 128, at most 1024
+    case 2: MOE_DLOGITS(2); break;
+    case 4: MOE_DLOGITS(4); break;
+    case 6: MOE_DLOGITS(6); break;
+    case 8: MOE_DLOGITS(8); break;
+    case 10: MOE_DLOGITS(10); break;
+    case 12: MOE_DLOGITS(12); break;
+    case 14: MOE_DLOGITS(14); break;
+    default: MOE_DLOGITS(16); break;
+  }
+#undef MOE_DLOGITS
   tr.mark(st, 1);
   hipLaunchKernelGGL((k_router_dx<Cfg>), dim3(((a.T + Cfg::BM - 1) / Cfg::BM) * (a.d / Cfg::BN)),
                      dim3(Cfg::kThreads), 0, st, dlp, static_cast<const T*>(a.Wr),
