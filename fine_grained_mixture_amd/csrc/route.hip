@@ -105,12 +105,20 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
   const int sub = tid & (kTopkLanes - 1), tl = tid / kTopkLanes;
   const int t = blockIdx.x * kTopkTokens + tl;
   const bool valid = t < T;
-  const float* row = logits + int64_t(valid ? t : 0) * E;
+  // the token's logits through a buffer descriptor over its row: positions
+  // past E read 0 (and are masked), so all EPL loads are issued together
+  const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(logits + int64_t(valid ? t : 0) * E), 0, E * 4, 0x00020000);
+  float lv[EPL];     // this lane's logits
   uint32_t ok[EPL];  // ordered logits of this lane's experts (0: none)
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    lv[j] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rrow, uint32_t(sub + kTopkLanes * j) * 4u, 0, 0));
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = sub + kTopkLanes * j;
-    ok[j] = (valid && e < E) ? ordered_f32(row[e]) : 0u;
+    ok[j] = (valid && e < E) ? ordered_f32(lv[j]) : 0u;
   }
   uint64_t taken = 0ull;
   double m = 0.0;
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = sub + kTopkLanes * j;
-    ex[j] = (valid && e < E) ? exp(double(row[e]) - m) : 0.0;
+    ex[j] = (valid && e < E) ? exp(double(lv[j]) - m) : 0.0;
     z += ex[j];
   }
 #pragma unroll
