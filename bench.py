@@ -402,8 +402,10 @@ def main():
         kernels[k] = {"us": round(t * 1e3, 2)}
         if fk:
             kernels[k]["tflops"] = round(fk / (t / 1e3) / 1e12, 1)
+            kernels[k]["mfma_frac"] = round(fk / (t / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 3)
         if bk:
             kernels[k]["gbs"] = round(bk / (t / 1e3) / 1e9, 1)
+            kernels[k]["hbm_frac"] = round(bk / (t / 1e3) / 1e9 / PEAK_HBM_GBS, 3)
 
     out = {
         "metric": "MoE layer fwd+bwd TFLOPS (bf16) + % MFMA peak, T=16k d=1536 E=128 K=8",
