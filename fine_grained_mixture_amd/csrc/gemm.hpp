@@ -14,9 +14,10 @@
 //                  the weights along their columns, and both operands of the
 //                  varlen-K weight-gradient GEMMs (rows = the expert's slots).
 //
-// DMA.  global_load_lds_dwordx4 copies 16 B per lane and places lane L's
+// DMA.  buffer_load_dwordx4 ... lds copies 16 B per lane and places lane L's
 // bytes at LDS base + 16 L, so one wave instruction fills 1 KB of a tile
-// contiguously while every lane may read any global address (the gather).
+// contiguously while every lane may read any address of the buffer (the
+// gather).
 // Tiles are unpadded; bank conflicts are avoided by XOR-swizzling the 16-byte
 // chunks of each row (the lane that fills a physical chunk fetches the
 // logical chunk that belongs there):
