@@ -105,11 +105,20 @@ def cpu_baseline(sh, inp, mode, target_s=15.0):
     }
 
 
-def measure(sh, mode, steps, warmup, dev, T=None):
+def _pct(v):
+    v = np.asarray(v)
+    return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+            "p90": round(float(np.percentile(v, 90)), 4)}
+
+
+def measure(sh, mode, steps, warmup, dev, T=None, stats=False):
     """Times `steps` route+fwd+bwd steps of layer `sh` (T tokens if given) in
     routing mode `mode` after `warmup` untimed ones.  Returns the mean step
     time, the mean time of every kernel (trace events on the stream), the
-    slot count S and the number of 128-row M tiles."""
+    slot count S and the number of 128-row M tiles.  With `stats`, also the
+    median / p10 / p90 of single steps, warm (back to back) and cold (a
+    512 MiB buffer written before each step, outside its timing, so that
+    no input is left in L2 or the Infinity Cache)."""
     inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0, T=T)
     T = sh.T if T is None else T
     X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
@@ -164,8 +173,24 @@ def measure(sh, mode, steps, warmup, dev, T=None):
         d = [a.elapsed_time(b) for group in (e_r, e_f, e_b) for a, b in zip(group, group[1:])]
         per += np.array(d)
     per /= steps
-    return {"ms": ms, "per_ms": per, "S": int(rt.totals[0].item()),
-            "tiles": int(rt.totals[1].item())}
+    out = {"ms": ms, "per_ms": per, "S": int(rt.totals[0].item()),
+           "tiles": int(rt.totals[1].item())}
+    if stats:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for cold in (False, True):
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(steps)]
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(pairs):
+                if cold:
+                    scratch.fill_(i & 255)
+                a.record(stream)
+                step()
+                b.record(stream)
+            torch.cuda.synchronize()
+            out["cold" if cold else "warm"] = _pct([a.elapsed_time(b) for a, b in pairs])
+        del scratch
+    return out
 
 
 def measure_router(sh, steps, warmup, dev):
@@ -369,7 +394,7 @@ def main():
         vendor_gemms(dev, args.steps, args.warmup, args.config)
         return
     sh = SHAPES[args.config]
-    r = measure(sh, args.mode, args.steps, args.warmup, dev)
+    r = measure(sh, args.mode, args.steps, args.warmup, dev, stats=True)
     ms, per, names = r["ms"], r["per_ms"], KERNEL_NAMES
     S = r["S"]
     flops = sh.flops
@@ -427,11 +452,22 @@ def main():
         # 18 n d per slot actually routed, and per row executed (whole tiles)
         "useful_tflops": 18 * S * sh.n * sh.d / (ms / 1e3) / 1e12,
         "executed_tflops": 18 * r["tiles"] * moe.TILE_M * sh.n * sh.d / (ms / 1e3) / 1e12,
+        # single steps: back to back (warm) and after evicting L2 and the
+        # Infinity Cache (cold), ms
+        "step_ms": {"warm": r["warm"], "cold": r["cold"]},
         "roofline": roof,
         "kernels_us": kernels,
         # outside the metric's step (its FLOPs are not in 18 T n K d)
         "router": router_line(sh, measure_router(sh, args.steps, args.warmup, dev)),
     }
+    if args.mode != "tc":
+        # token choice on the same inputs: the padding its tiles execute
+        t = measure(sh, "tc", args.steps, args.warmup, dev)
+        fl = 18 * sh.n * sh.d / (t["ms"] / 1e3) / 1e12
+        out["tc"] = {"ms_per_step": round(t["ms"], 4), "slots": t["S"],
+                     "executed_rows": t["tiles"] * moe.TILE_M,
+                     "useful_tflops": round(t["S"] * fl, 1),
+                     "executed_tflops": round(t["tiles"] * moe.TILE_M * fl, 1)}
     if not args.no_cpu_baseline:
         inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)  # the same seeded inputs
         out["cpu_baseline"] = cpu_baseline(sh, inp, args.mode)
