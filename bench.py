@@ -348,8 +348,8 @@ def vendor_gemms(dev, steps, warmup, config):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
     ap.add_argument("--mode", default="tr", choices=sorted(moe.ROUTE_MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
