@@ -353,6 +353,9 @@ def main():
     ap.add_argument("--config", default="7b", choices=sorted(SHAPES))
     ap.add_argument("--mode", default="tr", choices=sorted(moe.ROUTE_MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed and traced steps of --mode (no single-step statistics, "
+                         "no token-choice line): what the profiler runs")
     ap.add_argument("--granularity", action="store_true",
                     help="instead of the benchmark line: iso-FLOP sweep over d/n = 2, 4, 8, 16 "
                          "(one JSON line per point)")
@@ -394,7 +397,7 @@ def main():
         vendor_gemms(dev, args.steps, args.warmup, args.config)
         return
     sh = SHAPES[args.config]
-    r = measure(sh, args.mode, args.steps, args.warmup, dev, stats=True)
+    r = measure(sh, args.mode, args.steps, args.warmup, dev, stats=not args.no_extras)
     ms, per, names = r["ms"], r["per_ms"], KERNEL_NAMES
     S = r["S"]
     flops = sh.flops
@@ -454,13 +457,13 @@ def main():
         "executed_tflops": 18 * r["tiles"] * moe.TILE_M * sh.n * sh.d / (ms / 1e3) / 1e12,
         # single steps: back to back (warm) and after evicting L2 and the
         # Infinity Cache (cold), ms
-        "step_ms": {"warm": r["warm"], "cold": r["cold"]},
+        "step_ms": {"warm": r.get("warm"), "cold": r.get("cold")},
         "roofline": roof,
         "kernels_us": kernels,
         # outside the metric's step (its FLOPs are not in 18 T n K d)
         "router": router_line(sh, measure_router(sh, args.steps, args.warmup, dev)),
     }
-    if args.mode != "tc":
+    if args.mode != "tc" and not args.no_extras:
         # token choice on the same inputs: the padding its tiles execute
         t = measure(sh, "tc", args.steps, args.warmup, dev)
         fl = 18 * sh.n * sh.d / (t["ms"] / 1e3) / 1e12
