@@ -286,14 +286,15 @@ def router_backward(p: Problem, X, Wr, logits, dS, rt: Routing, dX, out=None, ws
 class MoELayerFunction(torch.autograd.Function):
     """Autograd wrapper.  Saves exactly X and H (plus the routing metadata) for
     the backward; the router-facing gradient dS is left on the routing object
-    (``routing.dS``) because the router itself sits outside this layer."""
+    (``routing.dS``) because the router itself sits outside this layer.  The
+    draws of stochastic rounding (``round_rand``) are an input."""
 
     @staticmethod
-    def forward(ctx, X, W1, W2, logits, K, M_tile, mode):
+    def forward(ctx, X, W1, W2, logits, K, M_tile, mode, round_rand):
         T, d = X.shape
         E, _, n2 = W1.shape
         p = problem(T, d, n2 // 2, E, K, M_tile, X.dtype, mode)
-        rt = route(p, logits)
+        rt = route(p, logits, round_rand=round_rand)
         O, H = forward(p, X, W1, W2, rt)
         ctx.save_for_backward(X, H, W1, W2)
         ctx.moe = (p, rt)
@@ -305,11 +306,11 @@ class MoELayerFunction(torch.autograd.Function):
         p, rt = ctx.moe
         dX, dW1, dW2, dS = backward(p, dO.contiguous(), X, H, W1, W2, rt)
         rt.tensors["dS"] = dS
-        return dX, dW1, dW2, None, None, None, None
+        return dX, dW1, dW2, None, None, None, None, None
 
 
-def moe_layer(X, W1, W2, logits, K, M_tile, mode="tr"):
-    return MoELayerFunction.apply(X, W1, W2, logits, K, M_tile, mode)
+def moe_layer(X, W1, W2, logits, K, M_tile, mode="tr", round_rand=None):
+    return MoELayerFunction.apply(X, W1, W2, logits, K, M_tile, mode, round_rand)
 
 
 class MoERouterLayerFunction(torch.autograd.Function):

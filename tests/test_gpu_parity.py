@@ -170,6 +170,29 @@ def test_parity_full_oracle(name, dtype, mode):
     assert np.all(g["dW1"].numpy()[idle] == 0) and np.all(g["dW2"].numpy()[idle] == 0)
 
 
+def test_layer_autograd_matches_explicit_calls():
+    # moe_layer wires route -> fwd and bwd through autograd; with stochastic
+    # rounding (draws as an input) it must reproduce the explicit C-ABI calls
+    # bit for bit.
+    shape = SHAPES["small"]
+    dt = torch.bfloat16
+    inp = make_layer_inputs(shape, dtype=dt, seed=3)
+    dev = torch.device("cuda", 0)
+    X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
+    rr = round_rand_tensor(make_round_rand(shape.E, 3)).to(dev)
+    Xa, W1a, W2a = (t.clone().requires_grad_(True) for t in (X, W1, W2))
+    O = moe.moe_layer(Xa, W1a, W2a, lg, shape.K, shape.M, "tr_stochastic", round_rand=rr)
+    O.backward(dO)
+    p = moe.problem(shape.T, shape.d, shape.n, shape.E, shape.K, shape.M, dt, "tr_stochastic")
+    rt = moe.route(p, lg, round_rand=rr)
+    O2, H = moe.forward(p, X, W1, W2, rt)
+    dX, dW1, dW2, dS = moe.backward(p, dO, X, H, W1, W2, rt)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
+    for got, want in ((Xa.grad, dX), (W1a.grad, dW1), (W2a.grad, dW2)):
+        assert torch.equal(got, want)
+
+
 def test_deterministic():
     shape = SHAPES["small"]
     inp = make_layer_inputs(shape, dtype=torch.bfloat16, seed=1)
