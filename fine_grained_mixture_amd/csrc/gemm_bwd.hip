@@ -30,7 +30,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
     const T* __restrict__ dO, const T* __restrict__ W2, const T* __restrict__ H,
     T* __restrict__ dH, T* __restrict__ As, float* __restrict__ dS,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
-    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ slot_token,
     const float* __restrict__ slot_weight, const int32_t* __restrict__ totals, int d, int ntok) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   constexpr int BM = Cfg::BM, BN = Cfg::BN, WGN = Cfg::WGN;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dh(
   if (lin < 0) return;
   const int mt = lin / SUB;
   const int e = tile_expert[mt], row0 = tile_row[mt] + (lin % SUB) * BM;
-  const int rend = expert_offsets[e + 1];
+  const int rend = tile_end(tile_row, totals, mt, tile_row[mt]);
   if (row0 >= rend) return;
   const int tok0 = slot_token[row0];
 
@@ -193,7 +193,7 @@ template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
     const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
-    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
+    const int32_t* __restrict__ totals, int d,
     int n, int nslot) {
   static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
   const int mt = lin / NT, nt = lin % NT;
-  const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
+  const int e = tile_expert[mt], row0 = tile_row[mt];
+  const int rend = tile_end(tile_row, totals, mt, row0);
   const int j0 = nt * BN;
 
   const uint32_t hrow = uint32_t(n2) * sizeof(T);
@@ -466,7 +467,7 @@ void dh_launch(const LayerArgs& a, const void* dO, const void* W2, const void* H
   hipLaunchKernelGGL((k_dh<Cfg>), dim3(grid_for(a.tile_cap * (kTileM / Cfg::BM))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dO),
                      static_cast<const T*>(W2), static_cast<const T*>(H), static_cast<T*>(dH),
-                     static_cast<T*>(As), dS, a.tile_expert, a.tile_row, a.expert_offsets,
+                     static_cast<T*>(As), dS, a.tile_expert, a.tile_row,
                      a.slot_token, a.slot_weight, a.totals, a.d, a.T);
 }
 
@@ -496,7 +497,7 @@ void dxt_launch(const LayerArgs& a, const void* dH, const void* W1, void* dXt, h
   hipLaunchKernelGGL((k_dxt<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dH),
                      static_cast<const T*>(W1), static_cast<T*>(dXt), a.tile_expert, a.tile_row,
-                     a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
+                     a.totals, a.d, a.n, int(a.slot_cap));
 }
 
 // Tile configurations of the two weight-gradient kernels; f(CfgTag<Cfg>{})

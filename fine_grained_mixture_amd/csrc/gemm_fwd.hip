@@ -25,7 +25,7 @@ template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
     const T* __restrict__ X, const T* __restrict__ W1, T* __restrict__ H, T* __restrict__ Aact,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
-    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ slot_token,
+    const int32_t* __restrict__ slot_token,
     const int32_t* __restrict__ totals, int d, int n, int ntok) {
   static_assert(Cfg::PAIRED && Cfg::BM == kTileM, "paired 128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
@@ -34,7 +34,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_up_swiglu(
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
   const int mt = lin / NT, nt = lin % NT;
-  const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
+  const int e = tile_expert[mt], row0 = tile_row[mt];
+  const int rend = tile_end(tile_row, totals, mt, row0);
   const int j0 = nt * HALF, n2 = 2 * n;
   const int tok0 = slot_token[row0];
 
@@ -98,7 +99,7 @@ template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_down(
     const T* __restrict__ Aact, const T* __restrict__ W2, T* __restrict__ Y,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
-    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
+    const int32_t* __restrict__ totals, int d,
     int n, int nslot) {
   static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_down(
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
   const int mt = lin / NT, nt = lin % NT;
-  const int e = tile_expert[mt], row0 = tile_row[mt], rend = expert_offsets[e + 1];
+  const int e = tile_expert[mt], row0 = tile_row[mt];
+  const int rend = tile_end(tile_row, totals, mt, row0);
   const int j0 = nt * BN;
 
   const uint32_t arow = uint32_t(n) * sizeof(T);
@@ -140,7 +142,7 @@ void up_launch(const LayerArgs& a, const void* X, const void* W1, void* H, void*
   hipLaunchKernelGGL((k_up_swiglu<Cfg>), dim3(grid_for(a.tile_cap * (a.n / half))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
                      static_cast<const T*>(W1), static_cast<T*>(H), static_cast<T*>(Aact),
-                     a.tile_expert, a.tile_row, a.expert_offsets, a.slot_token, a.totals, a.d,
+                     a.tile_expert, a.tile_row, a.slot_token, a.totals, a.d,
                      a.n, a.T);
 }
 
@@ -150,7 +152,7 @@ void down_launch(const LayerArgs& a, const void* Aact, const void* W2, void* Y, 
   hipLaunchKernelGGL((k_down<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(Aact),
                      static_cast<const T*>(W2), static_cast<T*>(Y), a.tile_expert, a.tile_row,
-                     a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
+                     a.totals, a.d, a.n, int(a.slot_cap));
 }
 
 }  // namespace
