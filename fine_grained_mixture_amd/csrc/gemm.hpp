@@ -569,10 +569,6 @@ __device__ __forceinline__ void store_acc_staged(const Accum<Cfg>& acc, char* ld
   }
 }
 
-// Spreads `work` logical tiles over the 8 XCDs in contiguous chunks:
-// workgroups are dispatched round-robin over XCDs, so block b runs on XCD
-// b % 8; giving each XCD a contiguous range keeps neighbouring tiles (same
-// expert, same weight panel) in one L2.  Returns -1 for surplus blocks.
 // The end of the rows of M tile mt: the next tile's first row when it exists
 // (a later tile of the same expert, or the first row of the next expert that
 // has any), else S, capped at the tile's 128 rows.  Equal to the tile's
@@ -583,6 +579,10 @@ __device__ __forceinline__ int tile_end(const int32_t* __restrict__ tile_row,
   return min(row0 + kTileM, next);
 }
 
+// Spreads `work` logical tiles over the 8 XCDs in contiguous chunks:
+// workgroups are dispatched round-robin over XCDs, so block b runs on XCD
+// b % 8; giving each XCD a contiguous range keeps neighbouring tiles (same
+// expert, same weight panel) in one L2.  Returns -1 for surplus blocks.
 __device__ __forceinline__ int xcd_tile(int b, int work) {
   const int per = (work + 7) / 8;
   const int local = b / 8, xcd = b % 8;

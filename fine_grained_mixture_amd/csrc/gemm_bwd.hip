@@ -2,9 +2,9 @@
 //
 // SonicMoE ICLR-2026 notes (papernotes.org), key designs 2 and 3: only X, H
 // and the routing metadata survive the forward.  The dH kernel gathers dO
-// rows into its operand load and, in its epilogue, reloads H, recomputes
-// A = SwiGLU(H), and forms dS = <dA', A> together with dSwiGLU, so neither Y
-// nor dY is ever needed.  The weight gradients are varlen-K grouped GEMMs:
+// rows into its operand load and, in its epilogue, reads H (loaded before
+// the K loop where the registers allow), recomputes A = SwiGLU(H), and forms
+// dS = <dA', A> together with dSwiGLU, so neither Y nor dY is ever needed.  The weight gradients are varlen-K grouped GEMMs:
 // the contraction runs over each expert's own (gathered) token rows.
 //
 //   k_dh    dA' = dO[I_e] W2_e^T; dS, dH, s*A in the epilogue
