@@ -6,6 +6,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -51,15 +52,55 @@ void sizes_of(const moe_problem* p, moe_sizes_t* s) {
   s->ws_route = moe::RouteWs::make(p->T, p->E).total;
   // forward transients: A [slot_cap, n], Y [slot_cap, d]
   s->ws_fwd = align256(size_t(s->slot_cap * p->n * es)) + align256(size_t(s->slot_cap * p->d * es));
-  // backward transients: dH [slot_cap, 2n], s*A [slot_cap, n], then dX~
-  // [slot_cap, d], whose space the weight-gradient phase (chunk plans and
-  // fp32 partial sums) reuses once dX has been aggregated
+  // backward transients: dH [slot_cap, 2n], s*A [slot_cap, n], dX~
+  // [slot_cap, d], and the weight-gradient chunk plans and fp32 partial sums
+  // (their own space: the weight gradients run beside dX~ and its aggregation)
   const size_t vw = moe::varlen_ws_bytes(p->dtype == MOE_F32, int(p->d), int(p->n), int(p->E),
                                          s->slot_cap);
   s->ws_router = moe::router_dims(int(p->T), int(p->d), int(p->E), p->dtype == MOE_F32).ws_bytes;
   s->ws_bwd = align256(size_t(s->slot_cap * 2 * p->n * es)) +
               align256(size_t(s->slot_cap * p->n * es)) +
-              std::max(align256(size_t(s->slot_cap * p->d * es)), vw);
+              align256(size_t(s->slot_cap * p->d * es)) + vw;
+}
+
+// A second stream per device for the backward's weight gradients, and the
+// events that fork it from and join it to the caller's stream.  Created on
+// first use with the device current; kept until the process ends.  Work on
+// it is ordered only by those events, so one mutex covers each fork/join
+// sequence (the events are shared between calls).
+constexpr int kMaxDevices = 64;
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// Caller holds g_side_mu.
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& s = g_side[dev];
+  if (!s.stream) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (j) (void)hipEventDestroy(j);
+      if (f) (void)hipEventDestroy(f);
+      if (st) (void)hipStreamDestroy(st);
+      return e;
+    }
+    s.stream = st;
+    s.fork = f;
+    s.join = j;
+  }
+  *out = &s;
+  return hipSuccess;
 }
 
 bool routing_ok(const moe_routing* r) {
@@ -225,22 +266,50 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
   void* As = w + align256(size_t(s.slot_cap * 2 * p->n * es));
   void* dXt = static_cast<char*>(As) + align256(size_t(s.slot_cap * p->n * es));
 
+  void* vws = static_cast<char*>(dXt) + align256(size_t(s.slot_cap * p->d * es));
+
   tr.mark(sm, 0);
   hipError_t e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
   if (e != hipSuccess) return MOE_ERR_HIP;
   tr.mark(sm, 1);
-  e = moe::launch_dxt(a, dH, W1, dXt, sm);
+  if (tr.count > 0) {
+    // traced: every kernel in order on the caller's stream, so that each
+    // segment between two events times one kernel
+    e = moe::launch_dxt(a, dH, W1, dXt, sm);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    tr.mark(sm, 2);
+    e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    tr.mark(sm, 3);
+    e = moe::launch_dw1(a, X, dH, dW1, vws, sm);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    tr.mark(sm, 4);
+    e = moe::launch_dw2(a, As, dO, dW2, vws, sm);
+    tr.mark(sm, 5);
+    return hip_status(e);
+  }
+  // Untraced: dX~ and its aggregation on the caller's stream, and beside
+  // them dW1 then dW2 on the side stream.  Both chains need only dH / s*A,
+  // and neither writes what the other reads.  Running them together keeps
+  // the CUs out of step: one kernel's tiles store their outputs while the
+  // other's stream operands, instead of every CU storing at once.
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  e = side_stream(&side);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  tr.mark(sm, 2);
-  e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
+  e = hipEventRecord(side->fork, sm);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  tr.mark(sm, 3);
-  e = moe::launch_dw1(a, X, dH, dW1, dXt, sm);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  tr.mark(sm, 4);
-  e = moe::launch_dw2(a, As, dO, dW2, dXt, sm);
-  tr.mark(sm, 5);
-  return hip_status(e);
+  hipError_t e_main = moe::launch_dxt(a, dH, W1, dXt, sm);
+  if (e_main == hipSuccess) e_main = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
+  hipError_t e_side = moe::launch_dw1(a, X, dH, dW1, vws, side->stream);
+  if (e_side == hipSuccess) e_side = moe::launch_dw2(a, As, dO, dW2, vws, side->stream);
+  // join whatever was enqueued, so the caller's stream (or its capture) ends
+  // after both chains even on an error
+  hipError_t e_join = hipEventRecord(side->join, side->stream);
+  if (e_join == hipSuccess) e_join = hipStreamWaitEvent(sm, side->join, 0);
+  if (e_main != hipSuccess || e_side != hipSuccess || e_join != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 int moe_router_fwd(const moe_problem* p, const void* X, const void* Wr, float* logits,

@@ -27,10 +27,15 @@
  * Conventions for every entry point:
  *   - All buffer pointers are DEVICE pointers, allocated and owned by the
  *     caller.  The library never allocates or frees memory and keeps no
- *     device state between calls.
+ *     data between calls.  Its only state is, per device, one stream and
+ *     two events that moe_bwd creates on first use and keeps until the
+ *     process ends.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream).  No call synchronises the host or copies device data to
- *     the host.  Data-dependent sizes (slot count S, tile count) stay on the
+ *     the host.  Untraced, moe_bwd forks part of its work onto its own
+ *     stream and joins it back to `stream` (event record + wait) before
+ *     returning, so everything it enqueues completes before later work on
+ *     `stream`, and a capture of `stream` captures all of it.  Data-dependent sizes (slot count S, tile count) stay on the
  *     device in `moe_routing.totals`; kernels past them exit early.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     failure the call returns a negative moe_status and enqueues nothing.
@@ -188,6 +193,11 @@ int moe_fwd(const moe_problem *p, const void *X, const void *W1,
  * Outputs: dX [T, d], dW1 [E, d, 2n], dW2 [E, n, d] (experts without slots
  * get zeros), dS [slot_cap] fp32 with rows [0, S) valid.
  * ws: at least sizes.ws_bwd bytes.
+ * Order: dH first; then dX (dX-tilde, its aggregation) on `stream` and, on
+ * the library's second stream of this device, dW1 then dW2, joined back to
+ * `stream`.  With a trace, all five run in order on `stream` instead.
+ * Concurrent calls on one device share that stream (a mutex orders their
+ * fork/join); the results do not depend on which path ran.
  */
 int moe_bwd(const moe_problem *p, const void *dO, const void *X, const void *H,
             const void *W1, const void *W2, const moe_routing *r, void *dX,
