@@ -1,0 +1,81 @@
+"""GPU: the backward's two-stream schedule.
+
+Untraced, moe_bwd runs dW1 and dW2 on the library's own stream of the device,
+forked from the caller's stream after dH and joined back before it returns;
+traced, it runs every kernel in order on the caller's stream.  Both orders run
+the same kernels on the same inputs, so they must give the same bytes, also
+when the untraced call is captured into a HIP graph and replayed (the join
+makes the capture take in both branches).
+"""
+import sys
+
+import pytest
+import torch
+
+from fine_grained_mixture_amd import moe
+from fine_grained_mixture_amd.inputs import SHAPES, make_layer_inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dX", "dW1", "dW2", "dS")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def layer(name):
+    shape = SHAPES[name]
+    log(f"[streams] {name}: T={shape.T} d={shape.d} n={shape.n} E={shape.E} K={shape.K}")
+    inp = make_layer_inputs(shape, dtype=torch.bfloat16, seed=0)
+    dev = torch.device("cuda", 0)
+    p = moe.problem(shape.T, shape.d, shape.n, shape.E, shape.K, shape.M, torch.bfloat16, "tr")
+    X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
+    rt = moe.route(p, lg)
+    _, H = moe.forward(p, X, W1, W2, rt)
+    return p, (dO, X, H, W1, W2, rt)
+
+
+def same(a, b, S):
+    for x, y, name in zip(a, b, NAMES):
+        if name == "dS":
+            x, y = x[:S], y[:S]
+        assert torch.equal(x, y), f"{name} differs"
+
+
+def test_bwd_traced_and_forked_agree():
+    p, args = layer("small")
+    forked = [t.clone() for t in moe.backward(p, *args)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in events:
+        e.record()  # torch creates the HIP event on its first record
+    traced = moe.backward(p, *args, events=events)
+    torch.cuda.synchronize()
+    same(forked, traced, int(args[-1].totals[0]))
+
+
+def test_bwd_graph_replays_match_eager():
+    p, args = layer("small")
+    dev = args[0].device
+    s = moe.sizes(p)
+    ws = moe.workspace(s.ws_bwd, dev)
+    out = (torch.empty(p.T, p.d, dtype=torch.bfloat16, device=dev),
+           torch.empty(p.E, p.d, 2 * p.n, dtype=torch.bfloat16, device=dev),
+           torch.empty(p.E, p.n, p.d, dtype=torch.bfloat16, device=dev),
+           torch.empty(s.slot_cap, dtype=torch.float32, device=dev))
+    # eager first: it also creates the library's stream for this device
+    ref = [t.clone() for t in moe.backward(p, *args, out=out, ws=ws)]
+    torch.cuda.synchronize()
+    S = int(args[-1].totals[0])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.backward(p, *args, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in out:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[streams] replay {i}")
+        same(out, ref, S)
