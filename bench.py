@@ -111,14 +111,17 @@ def _pct(v):
             "p90": round(float(np.percentile(v, 90)), 4)}
 
 
-def measure(sh, mode, steps, warmup, dev, T=None, stats=False):
+def measure(sh, mode, steps, warmup, dev, T=None, stats=False, traced_only=False):
     """Times `steps` route+fwd+bwd steps of layer `sh` (T tokens if given) in
     routing mode `mode` after `warmup` untimed ones.  Returns the mean step
     time, the mean time of every kernel (trace events on the stream), the
     slot count S and the number of 128-row M tiles.  With `stats`, also the
     median / p10 / p90 of single steps, warm (back to back) and cold (a
     512 MiB buffer written before each step, outside its timing, so that
-    no input is left in L2 or the Infinity Cache)."""
+    no input is left in L2 or the Infinity Cache).  With `traced_only`, every
+    step (warm-up included) is traced and the step time is the traced one:
+    the profiler's run, whose per-kernel averages then cover exactly the
+    launches that `per_ms` times."""
     inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0, T=T)
     T = sh.T if T is None else T
     X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
@@ -148,26 +151,39 @@ def measure(sh, mode, steps, warmup, dev, T=None, stats=False):
         moe.forward(p, X, W1, W2, rt, out=(O, H), ws=ws_f, stream=stream, events=e_f)
         moe.backward(p, dO, X, H, W1, W2, rt, out=grads, ws=ws_b, stream=stream, events=e_b)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    # The step time comes from steps without trace events (an event record
-    # costs GPU time of its own: about 3 us each, 50 us per step); the
-    # per-kernel times come from the same number of traced steps right after.
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
-    evs = [(mk(len(moe.ROUTE_KERNELS) + 1), mk(len(moe.FWD_KERNELS) + 1),
-            mk(len(moe.BWD_KERNELS) + 1)) for _ in range(steps)]
+    def traced_events(k):
+        return [(mk(len(moe.ROUTE_KERNELS) + 1), mk(len(moe.FWD_KERNELS) + 1),
+                 mk(len(moe.BWD_KERNELS) + 1)) for _ in range(k)]
+
+    if traced_only:
+        # every launch traced (a traced backward runs its kernels in order), so
+        # a profiler's per-kernel averages cover the same launches as `per_ms`
+        for ev in traced_events(warmup):
+            step(ev)
+        torch.cuda.synchronize()
+    else:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        # The step time comes from steps without trace events (an event record
+        # costs GPU time of its own: about 3 us each, 50 us per step); the
+        # per-kernel times come from the same number of traced steps right
+        # after.
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / steps
+    evs = traced_events(steps)
     torch.cuda.synchronize()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
+    if traced_only:
+        ms = float(np.mean([e_r[0].elapsed_time(e_b[-1]) for e_r, _, e_b in evs]))
     per = np.zeros(len(KERNEL_NAMES))
     for e_r, e_f, e_b in evs:
         d = [a.elapsed_time(b) for group in (e_r, e_f, e_b) for a, b in zip(group, group[1:])]
@@ -356,6 +372,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed and traced steps of --mode (no single-step statistics, "
                          "no token-choice line): what the profiler runs")
+    ap.add_argument("--traced-only", action="store_true",
+                    help="every step traced (the backward then runs its kernels in order), "
+                         "step time from the traced steps: what the profiler runs, so that its "
+                         "per-kernel averages match the per-kernel times printed")
     ap.add_argument("--granularity", action="store_true",
                     help="instead of the benchmark line: iso-FLOP sweep over d/n = 2, 4, 8, 16 "
                          "(one JSON line per point)")
@@ -397,7 +417,8 @@ def main():
         vendor_gemms(dev, args.steps, args.warmup, args.config)
         return
     sh = SHAPES[args.config]
-    r = measure(sh, args.mode, args.steps, args.warmup, dev, stats=not args.no_extras)
+    r = measure(sh, args.mode, args.steps, args.warmup, dev,
+                stats=not (args.no_extras or args.traced_only), traced_only=args.traced_only)
     ms, per, names = r["ms"], r["per_ms"], KERNEL_NAMES
     S = r["S"]
     flops = sh.flops
@@ -458,12 +479,17 @@ def main():
         # single steps: back to back (warm) and after evicting L2 and the
         # Infinity Cache (cold), ms
         "step_ms": {"warm": r.get("warm"), "cold": r.get("cold")},
+        # how ms_per_step was timed: untraced steps (dW1/dW2 beside dX-tilde),
+        # or traced ones (every kernel in order, plus the events' own cost)
+        "timing": "traced" if args.traced_only else "untraced",
         "roofline": roof,
         "kernels_us": kernels,
-        # outside the metric's step (its FLOPs are not in 18 T n K d)
-        "router": router_line(sh, measure_router(sh, args.steps, args.warmup, dev)),
     }
-    if args.mode != "tc" and not args.no_extras:
+    if not args.traced_only:
+        # outside the metric's step (its FLOPs are not in 18 T n K d); its set-up
+        # runs one untraced layer step, which a profiler would count
+        out["router"] = router_line(sh, measure_router(sh, args.steps, args.warmup, dev))
+    if args.mode != "tc" and not (args.no_extras or args.traced_only):
         # token choice on the same inputs: the padding its tiles execute
         t = measure(sh, "tc", args.steps, args.warmup, dev)
         fl = 18 * sh.n * sh.d / (t["ms"] / 1e3) / 1e12
