@@ -197,7 +197,9 @@ int moe_fwd(const moe_problem *p, const void *X, const void *W1,
  * the library's second stream of this device, dW1 then dW2, joined back to
  * `stream`.  With a trace, all five run in order on `stream` instead.
  * Concurrent calls on one device share that stream (a mutex orders their
- * fork/join); the results do not depend on which path ran.
+ * fork/join); the results do not depend on which path ran.  The first
+ * untraced call on a device creates the stream and its two events, so make
+ * one such call before capturing `stream` into a graph.
  */
 int moe_bwd(const moe_problem *p, const void *dO, const void *X, const void *H,
             const void *W1, const void *W2, const moe_routing *r, void *dX,
