@@ -67,7 +67,9 @@ void sizes_of(const moe_problem* p, moe_sizes_t* s) {
 // events that fork it from and join it to the caller's stream.  Created on
 // first use with the device current; kept until the process ends.  Work on
 // it is ordered only by those events, so one mutex covers each fork/join
-// sequence (the events are shared between calls).
+// sequence (the events are shared between calls).  A caller's stream that
+// belongs to another device than the current one gets no side stream
+// (*out = nullptr): the call then runs in order on the caller's stream.
 constexpr int kMaxDevices = 64;
 struct SideStream {
   hipStream_t stream = nullptr;
@@ -77,11 +79,18 @@ std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
 // Caller holds g_side_mu.
-hipError_t side_stream(SideStream** out) {
+hipError_t side_stream(hipStream_t caller, SideStream** out) {
+  *out = nullptr;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (caller) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(caller, &sd);
+    if (e != hipSuccess) return e;
+    if (int(sd) != dev) return hipSuccess;
+  }
   SideStream& s = g_side[dev];
   if (!s.stream) {
     hipStream_t st = nullptr;
@@ -268,13 +277,20 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
 
   void* vws = static_cast<char*>(dXt) + align256(size_t(s.slot_cap * p->d * es));
 
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  if (tr.count == 0) {
+    lock.lock();
+    if (side_stream(sm, &side) != hipSuccess) return MOE_ERR_HIP;
+    if (!side) lock.unlock();
+  }
   tr.mark(sm, 0);
   hipError_t e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
   if (e != hipSuccess) return MOE_ERR_HIP;
   tr.mark(sm, 1);
-  if (tr.count > 0) {
-    // traced: every kernel in order on the caller's stream, so that each
-    // segment between two events times one kernel
+  if (!side) {
+    // traced (or no side stream): every kernel in order on the caller's
+    // stream, so that each segment between two events times one kernel
     e = moe::launch_dxt(a, dH, W1, dXt, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 2);
@@ -293,10 +309,6 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
   // and neither writes what the other reads.  Running them together keeps
   // the CUs out of step: one kernel's tiles store their outputs while the
   // other's stream operands, instead of every CU storing at once.
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* side = nullptr;
-  e = side_stream(&side);
-  if (e != hipSuccess) return MOE_ERR_HIP;
   e = hipEventRecord(side->fork, sm);
   if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -195,7 +195,8 @@ int moe_fwd(const moe_problem *p, const void *X, const void *W1,
  * ws: at least sizes.ws_bwd bytes.
  * Order: dH first; then dX (dX-tilde, its aggregation) on `stream` and, on
  * the library's second stream of this device, dW1 then dW2, joined back to
- * `stream`.  With a trace, all five run in order on `stream` instead.
+ * `stream`.  With a trace, or when `stream` belongs to another device than
+ * the current one, all five run in order on `stream` instead.
  * Concurrent calls on one device share that stream (a mutex orders their
  * fork/join); the results do not depend on which path ran.  The first
  * untraced call on a device creates the stream and its two events, so make
