@@ -43,8 +43,9 @@ def same(a, b, S):
         assert torch.equal(x, y), f"{name} differs"
 
 
-def test_bwd_traced_and_forked_agree():
-    p, args = layer("small")
+@pytest.mark.parametrize("name", ["small", "7b"])
+def test_bwd_traced_and_forked_agree(name):
+    p, args = layer(name)
     forked = [t.clone() for t in moe.backward(p, *args)]
     events = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for e in events:
