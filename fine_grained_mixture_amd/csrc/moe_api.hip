@@ -68,8 +68,9 @@ void sizes_of(const moe_problem* p, moe_sizes_t* s) {
 // first use with the device current; kept until the process ends.  Work on
 // it is ordered only by those events, so one mutex covers each fork/join
 // sequence (the events are shared between calls).  A caller's stream that
-// belongs to another device than the current one gets no side stream
-// (*out = nullptr): the call then runs in order on the caller's stream.
+// belongs to another device than the current one (or whose device cannot be
+// read) gets no side stream (*out = nullptr): the call then runs in order on
+// the caller's stream.
 constexpr int kMaxDevices = 64;
 struct SideStream {
   hipStream_t stream = nullptr;
@@ -86,9 +87,12 @@ hipError_t side_stream(hipStream_t caller, SideStream** out) {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   if (caller) {
+    // a stream whose device cannot be read is treated as another device's
     hipDevice_t sd = 0;
-    e = hipStreamGetDevice(caller, &sd);
-    if (e != hipSuccess) return e;
+    if (hipStreamGetDevice(caller, &sd) != hipSuccess) {
+      (void)hipGetLastError();
+      return hipSuccess;
+    }
     if (int(sd) != dev) return hipSuccess;
   }
   SideStream& s = g_side[dev];
