@@ -80,3 +80,50 @@ def test_bwd_graph_replays_match_eager():
         torch.cuda.synchronize()
         log(f"[streams] replay {i}")
         same(out, ref, S)
+
+
+def test_step_graph_replays_match_eager():
+    """The whole step (route, forward, backward) captured once and replayed,
+    as the benchmark times it, reproduces the eager step's bytes."""
+    shape = SHAPES["small"]
+    log(f"[streams] step graph: small T={shape.T}")
+    inp = make_layer_inputs(shape, dtype=torch.bfloat16, seed=0)
+    dev = torch.device("cuda", 0)
+    p = moe.problem(shape.T, shape.d, shape.n, shape.E, shape.K, shape.M, torch.bfloat16, "tr")
+    X, W1, W2, lg, dO = (inp[k].to(dev) for k in ("X", "W1", "W2", "logits", "dO"))
+    s = moe.sizes(p)
+    rt = moe.alloc_routing(p, dev)
+    ws_r, ws_f, ws_b = (moe.workspace(n, dev) for n in (s.ws_route, s.ws_fwd, s.ws_bwd))
+    O = torch.empty(p.T, p.d, dtype=torch.bfloat16, device=dev)
+    H = torch.empty(s.slot_cap, 2 * p.n, dtype=torch.bfloat16, device=dev)
+    grads = (torch.empty(p.T, p.d, dtype=torch.bfloat16, device=dev),
+             torch.empty(p.E, p.d, 2 * p.n, dtype=torch.bfloat16, device=dev),
+             torch.empty(p.E, p.n, p.d, dtype=torch.bfloat16, device=dev),
+             torch.empty(s.slot_cap, dtype=torch.float32, device=dev))
+
+    def step():
+        moe.route(p, lg, rt=rt, ws=ws_r)
+        moe.forward(p, X, W1, W2, rt, out=(O, H), ws=ws_f)
+        moe.backward(p, dO, X, H, W1, W2, rt, out=grads, ws=ws_b)
+
+    def outputs():
+        S = int(rt.totals[0])
+        return [t.clone() for t in (rt.totals, rt.slot_token[:S], rt.token_slots[:S], O, H[:S],
+                                    grads[0], grads[1], grads[2], grads[3][:S])]
+
+    step()  # eager first: it also creates the library's stream for this device
+    torch.cuda.synchronize()
+    want = outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in (O, H, *grads, rt.slot_token, rt.token_slots):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[streams] step replay {i}")
+        for a, b in zip(outputs(), want):
+            assert torch.equal(a, b)
