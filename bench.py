@@ -64,12 +64,25 @@ def cpu_baseline(sh, inp, mode, target_s=15.0):
     """fp64 oracle on a sample of experts: route (full), forward, backward."""
     from oracle import moe_oracle as orc
 
+    threads, blas = os.cpu_count(), "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = sum(i.get("num_threads", 0) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or os.cpu_count()
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            threads = sum(i.get("num_threads", 0) for i in libs) or threads
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} "
+                             f"({i.get('num_threads')} threads)" for i in libs)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        pass
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     a = {k: v.float().numpy().astype(np.float64) for k, v in inp.items() if k != "logits"}
     logits = inp["logits"].numpy()
     t0 = time.perf_counter()
@@ -98,6 +111,8 @@ def cpu_baseline(sh, inp, mode, target_s=15.0):
         "value": flops / dt / 1e12,
         "unit": "TFLOPS",
         "cores": int(threads),
+        "cpu_model": cpu_model,
+        "blas": blas,
         "kind": "oracle",
         "sample": f"fp64 numpy oracle: full routing ({t_route:.2f} s) + forward and minimal "
                   f"backward over {ne} of {sh.E} experts ({S_s} of {rt.S} slots, "
@@ -111,11 +126,14 @@ def _pct(v):
             "p90": round(float(np.percentile(v, 90)), 4)}
 
 
-def measure(sh, mode, steps, warmup, dev, T=None, stats=False, traced_only=False):
+def measure(sh, mode, steps, warmup, dev, T=None, stats=False, traced_only=False, cold=False):
     """Times `steps` route+fwd+bwd steps of layer `sh` (T tokens if given) in
     routing mode `mode` after `warmup` untimed ones.  Returns the mean step
     time, the mean time of every kernel (trace events on the stream), the
-    slot count S and the number of 128-row M tiles.  With `stats`, also the
+    slot count S and the number of 128-row M tiles.  The mean step time is
+    that of back-to-back steps (`ms_warm`), or with `cold` that of steps each
+    timed alone after a 512 MiB buffer was written outside its timing
+    (`ms_cold`: no input left in L2 or the Infinity Cache).  With `stats`, also the
     median / p10 / p90 of single steps, warm (back to back) and cold (a
     512 MiB buffer written before each step, outside its timing, so that
     no input is left in L2 or the Infinity Cache).  With `traced_only`, every
@@ -176,7 +194,21 @@ def measure(sh, mode, steps, warmup, dev, T=None, stats=False, traced_only=False
             step()
         stop.record(stream)
         torch.cuda.synchronize()
-        ms = start.elapsed_time(stop) / steps
+        ms_warm = start.elapsed_time(stop) / steps
+        ms = ms_warm
+        if cold:
+            scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(steps)]
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(pairs):
+                scratch.fill_(i & 255)  # evicts L2 and the Infinity Cache, untimed
+                a.record(stream)
+                step()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+            del scratch
     evs = traced_events(steps)
     torch.cuda.synchronize()
     for i in range(steps):
@@ -191,6 +223,8 @@ def measure(sh, mode, steps, warmup, dev, T=None, stats=False, traced_only=False
     per /= steps
     out = {"ms": ms, "per_ms": per, "S": int(rt.totals[0].item()),
            "tiles": int(rt.totals[1].item())}
+    if not traced_only:
+        out["ms_warm"] = ms_warm
     if stats:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         for cold in (False, True):
@@ -287,14 +321,41 @@ def sweep(dev, steps, warmup):
                               "executed_tflops": round(rows * per_row, 1)}), flush=True)
 
 
+def requested_bytes(dev):
+    """Bytes of live tensors as requested from the torch allocator."""
+    return torch.cuda.memory_stats(dev)["requested_bytes.all.current"]
+
+
+def saved_activation_bytes(sh, mode, dev):
+    """Device bytes MoELayerFunction holds for its backward after its forward,
+    measured with the torch allocator (bytes of live tensors still requested
+    beyond the inputs and the output O): H with exactly S rows, and the routing
+    metadata.  X, an input, is kept by reference.  Returns (X bytes, H
+    bytes, metadata bytes, measured bytes held, S)."""
+    inp = make_layer_inputs(sh, dtype=torch.bfloat16, seed=0)
+    X, W1, W2 = (inp[k].to(dev).requires_grad_(True) for k in ("X", "W1", "W2"))
+    lg = inp["logits"].to(dev)
+    torch.cuda.synchronize()
+    before = requested_bytes(dev)
+    O = moe.moe_layer(X, W1, W2, lg, sh.K, sh.M, mode)
+    torch.cuda.synchronize()
+    held = requested_bytes(dev) - before - O.numel() * O.element_size()
+    _, H, _, _, _ = O.grad_fn.saved_tensors
+    _, rt = O.grad_fn.moe
+    meta = sum(t.numel() * t.element_size() for t in rt.tensors.values())
+    return (X.numel() * X.element_size(), H.numel() * H.element_size(), meta, held, rt.S)
+
+
 def granularity_sweep(dev, steps, warmup):
     """Iso-FLOP sweep over granularity G = d/n at d = 1024, T = 16384 and
     sparsity K/E = 1/16, with nK = 1024 fixed (so 18 T n K d is the same at
     every point): G = 2, 4, 8, 16 -> (n, K, E) = (512, 2, 32), (256, 4, 64),
     (128, 8, 128), (64, 16, 256); token rounding.  One JSON line per point:
-    step time, TFLOPS, the forward arithmetic intensity, and the bytes kept
-    for the backward by this layer (X, H) against a backward that caches
-    every intermediate (plus gathered X, A, Y)."""
+    step time, TFLOPS, the forward arithmetic intensity, the activation bytes
+    the layer's autograd op was measured to hold for its backward (X, H and
+    the routing metadata), and, for comparison, what a backward that caches
+    every intermediate would keep (the gathered X rows, H, A and Y on top of
+    X: a formula, that backward is not built)."""
     from fine_grained_mixture_amd.inputs import LayerShape
     from fine_grained_mixture_amd.profiling import activation_bytes, arithmetic_intensity
 
@@ -305,60 +366,16 @@ def granularity_sweep(dev, steps, warmup):
         E = 16 * K
         sh = LayerShape(f"g{G}", T, d, n, E, K, 128, "fan_in", "normal_bias")
         r = measure(sh, "tr", steps, warmup, dev)
-        mem = activation_bytes(T, d, n, K, r["S"])
-        print(json.dumps({"G": G, "n": n, "K": K, "E": E, "T": T, "d": d,
+        xb, hb, meta, held, S = saved_activation_bytes(sh, "tr", dev)
+        print(json.dumps({"G": G, "n": n, "K": K, "E": E, "T": T, "d": d, "S": S,
                           "ms_per_step": round(r["ms"], 4),
                           "tflops": round(sh.flops / (r["ms"] / 1e3) / 1e12, 1),
                           "arithmetic_intensity": round(arithmetic_intensity(T, d, n, K, E), 1),
-                          "saved_bytes_minimal": mem["minimal"],
-                          "saved_bytes_caching": mem["caching"]}), flush=True)
-
-
-def vendor_gemms(dev, steps, warmup, config):
-    """hipBLASLt (torch.mm / torch.bmm, bf16, contiguous operands) at the
-    GEMM shapes of one layer step with S = T K slots, as dense GEMMs without
-    gather or fused epilogue (bmm: one batch per expert of S / E rows).  A
-    reference point for the grouped kernels, not part of the path.  One JSON
-    line per shape."""
-    sh = SHAPES[config]
-    S, d, n, E = sh.T * sh.K, sh.d, sh.n, sh.E
-    Se = S // E
-    bf = torch.bfloat16
-    g = torch.Generator(device=dev)
-    g.manual_seed(0)
-
-    def rnd(*shape):
-        return torch.randn(*shape, device=dev, dtype=bf, generator=g)
-
-    cases = [
-        ("up mm [S,d]x[d,2n]", (rnd(S, d), rnd(d, 2 * n)), torch.mm, 2 * S * d * 2 * n),
-        ("down mm [S,n]x[n,d]", (rnd(S, n), rnd(n, d)), torch.mm, 2 * S * n * d),
-        ("dxt mm [S,2n]x[2n,d]", (rnd(S, 2 * n), rnd(2 * n, d)), torch.mm, 2 * S * 2 * n * d),
-        ("dA' mm [S,d]x[d,n]", (rnd(S, d), rnd(d, n)), torch.mm, 2 * S * d * n),
-        ("up bmm E x [S/E,d]x[d,2n]", (rnd(E, Se, d), rnd(E, d, 2 * n)), torch.bmm,
-         2 * S * d * 2 * n),
-        ("down bmm E x [S/E,n]x[n,d]", (rnd(E, Se, n), rnd(E, n, d)), torch.bmm, 2 * S * n * d),
-        ("dxt bmm E x [S/E,2n]x[2n,d]", (rnd(E, Se, 2 * n), rnd(E, 2 * n, d)), torch.bmm,
-         2 * S * 2 * n * d),
-        ("dW1 bmm E x [d,S/E]x[S/E,2n]", (rnd(E, d, Se), rnd(E, Se, 2 * n)), torch.bmm,
-         2 * S * d * 2 * n),
-        ("dW2 bmm E x [n,S/E]x[S/E,d]", (rnd(E, n, Se), rnd(E, Se, d)), torch.bmm,
-         2 * S * n * d),
-    ]
-    for name, (a, b), fn, fl in cases:
-        for _ in range(warmup):
-            fn(a, b)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(steps):
-            fn(a, b)
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / steps
-        print(json.dumps({"gemm": name, "config": config, "us": round(ms * 1e3, 1),
-                          "tflops": round(fl / (ms / 1e3) / 1e12, 1)}), flush=True)
-        del a, b
+                          "saved_bytes_measured": xb + held,
+                          "saved_x_h_bytes": xb + hb, "saved_metadata_bytes": meta,
+                          "saved_bytes_2Td_4TKn": 2 * T * d + 4 * T * K * n,
+                          "saved_bytes_caching_formula":
+                              activation_bytes(T, d, n, K, S)["caching"]}), flush=True)
 
 
 def main():
@@ -382,9 +399,6 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: TC vs token rounding at 1, 2, 4 and 8 "
                          "M-tiles of tokens per expert (one JSON line per point)")
-    ap.add_argument("--vendor-gemms", action="store_true",
-                    help="instead of the benchmark line: hipBLASLt (torch.mm / bmm) at the "
-                         "layer's GEMM shapes, dense and contiguous, as a reference point")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (known HBM "
                          "traffic: 1 GiB read + 1 GiB written per launch), to scale the "
@@ -413,12 +427,10 @@ def main():
     if args.granularity:
         granularity_sweep(dev, args.steps, args.warmup)
         return
-    if args.vendor_gemms:
-        vendor_gemms(dev, args.steps, args.warmup, args.config)
-        return
     sh = SHAPES[args.config]
     r = measure(sh, args.mode, args.steps, args.warmup, dev,
-                stats=not (args.no_extras or args.traced_only), traced_only=args.traced_only)
+                stats=not (args.no_extras or args.traced_only), traced_only=args.traced_only,
+                cold=not args.traced_only)
     ms, per, names = r["ms"], r["per_ms"], KERNEL_NAMES
     S = r["S"]
     flops = sh.flops
@@ -480,8 +492,12 @@ def main():
         # Infinity Cache (cold), ms
         "step_ms": {"warm": r.get("warm"), "cold": r.get("cold")},
         # how ms_per_step was timed: untraced steps (dW1/dW2 beside dX-tilde),
-        # or traced ones (every kernel in order, plus the events' own cost)
-        "timing": "traced" if args.traced_only else "untraced",
+        # each after L2 and the Infinity Cache were evicted (cold), or traced
+        # back-to-back ones (every kernel in order, plus the events' own cost)
+        "timing": "traced" if args.traced_only else "untraced, cold",
+        # the same untraced steps back to back (inputs partly cached)
+        "warm": None if args.traced_only else {
+            "ms_per_step": r["ms_warm"], "tflops": flops / (r["ms_warm"] / 1e3) / 1e12},
         "roofline": roof,
         "kernels_us": kernels,
     }
@@ -491,7 +507,7 @@ def main():
         out["router"] = router_line(sh, measure_router(sh, args.steps, args.warmup, dev))
     if args.mode != "tc" and not (args.no_extras or args.traced_only):
         # token choice on the same inputs: the padding its tiles execute
-        t = measure(sh, "tc", args.steps, args.warmup, dev)
+        t = measure(sh, "tc", args.steps, args.warmup, dev, cold=True)
         fl = 18 * sh.n * sh.d / (t["ms"] / 1e3) / 1e12
         out["tc"] = {"ms_per_step": round(t["ms"], 4), "slots": t["S"],
                      "executed_rows": t["tiles"] * moe.TILE_M,

@@ -43,14 +43,12 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False, jobs: int | None = None, defines=(), lib: str = LIB,
+def build(verbose: bool = False, jobs: int | None = None, lib: str = LIB,
           objdir: str = OBJDIR) -> str:
-    """Compiles every source and links `lib`.  `defines` are extra -D
-    options (e.g. MOE_TILE_VARIANT=n to pick another GEMM tile shape)."""
+    """Compiles every source and links `lib`."""
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
-    dflags = [f"-D{d}" for d in defines]
-    cmds = [[HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, s), "-o", o]
+    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o]
             for s, o in zip(SOURCES, objs)]
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:

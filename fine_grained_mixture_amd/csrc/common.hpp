@@ -149,6 +149,16 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 template <class T>
 __host__ __device__ constexpr T cdiv(T a, T b) { return (a + b - 1) / b; }
 
+// A router score brought into the finite fp32 range: NaN and -inf become
+// -FLT_MAX, +inf becomes +FLT_MAX.  Routing and the gate's backward see the
+// logits only through this, so inputs outside the real numbers still get one
+// ranking (a NaN below every number) and a finite softmax.
+__device__ __forceinline__ float finite_logit(float x) {
+  constexpr float kMax = 3.40282347e+38f;
+  if (__builtin_isnan(x)) return -kMax;
+  return x > kMax ? kMax : (x < -kMax ? -kMax : x);
+}
+
 // Routing workspace layout (byte offsets), shared by the host code and the
 // routing kernels.
 struct RouteWs {

@@ -87,5 +87,9 @@ struct RouterBwdArgs {
   void *dWr, *dX, *ws;
 };
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t st, const TraceHook& tr);
+// dlogits alone (the gate's softmax backward), no workspace.
+hipError_t launch_gate_bwd(const float* logits, const float* dS, const int32_t* token_offsets,
+                           const int32_t* token_slots, const int32_t* expert_offsets,
+                           float* dlogits, int T, int E, hipStream_t st);
 
 }  // namespace moe

@@ -21,6 +21,23 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t elem_size(const moe_problem* p) { return p->dtype == MOE_F32 ? 4 : 2; }
 
+// Slots any routing of the problem can produce.  Token choice keeps exactly
+// T*K pairs; the rounding subroutines move each expert's count to a multiple
+// of M_tile: nearest pads only when the upward gap is strictly smaller than
+// M_tile/2 (so by at most floor((M_tile-1)/2) slots), up and stochastic pad
+// by at most M_tile-1, down never pads.  No expert holds more than T tokens.
+int64_t slot_bound(const moe_problem* p) {
+  const int64_t tk = p->T * p->K, M = p->M_tile;
+  int64_t pad = 0;
+  switch (p->mode) {
+    case MOE_ROUTE_TR: pad = (M - 1) / 2; break;
+    case MOE_ROUTE_TR_UP:
+    case MOE_ROUTE_TR_STOCHASTIC: pad = M - 1; break;
+    default: pad = 0; break;  // token choice, round down
+  }
+  return std::min(tk + p->E * pad, p->T * p->E);
+}
+
 int check_problem(const moe_problem* p) {
   if (!p) return MOE_ERR_INVALID;
   if (p->T < 1 || p->d < 1 || p->n < 1 || p->E < 1 || p->K < 1 || p->M_tile < 1)
@@ -32,22 +49,33 @@ int check_problem(const moe_problem* p) {
   if (p->d % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (p->n != 64 && p->n != 128 && p->n != 256 && p->n != 384 && p->n != 512)
     return MOE_ERR_UNSUPPORTED;
-  // Kernels index rows with 32-bit element offsets, and the GEMM operand
+  // Kernels index rows with 32-bit element offsets, and the GEMM and routing
   // loads address each array through a buffer descriptor with a 32-bit byte
-  // extent.
-  const int64_t slot_cap = p->T * p->K + p->E * p->M_tile;
+  // extent: every such array must stay below 4 GiB.
   if (p->T > INT_MAX / 64 || p->E > INT_MAX / p->T) return MOE_ERR_UNSUPPORTED;
+  const int64_t slot_cap = slot_bound(p);
   if (p->T * p->d >= INT_MAX || slot_cap * 2 * p->n >= INT_MAX || slot_cap * p->d >= INT_MAX)
     return MOE_ERR_UNSUPPORTED;
   const int64_t es = p->dtype == MOE_F32 ? 4 : 2, lim = int64_t(UINT32_MAX);
-  if (p->T * p->d * es > lim || slot_cap * 2 * p->n * es > lim || slot_cap * p->d * es > lim)
-    return MOE_ERR_UNSUPPORTED;
+  const int64_t Ep = (p->E + 127) / 128 * 128;  // row length of the router's padded dl copy
+  const int64_t extents[] = {
+      p->T * p->d * es,           // X, dO, O, dX
+      slot_cap * 2 * p->n * es,   // H, dH
+      slot_cap * p->d * es,       // Y, dX-tilde
+      p->d * 2 * p->n * es,       // one expert of W1 / dW1
+      p->n * p->d * es,           // one expert of W2 / dW2
+      p->E * p->d * es,           // Wr, dWr
+      p->T * Ep * es,             // the router's padded dl copy
+      p->T * p->E * 4,            // logits, dlogits
+  };
+  for (int64_t x : extents)
+    if (x > lim) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 void sizes_of(const moe_problem* p, moe_sizes_t* s) {
   const int64_t es = elem_size(p);
-  s->slot_cap = p->T * p->K + p->E * p->M_tile;
+  s->slot_cap = slot_bound(p);
   s->tile_cap = cdiv<int64_t>(s->slot_cap, moe::kTileM) + p->E;
   s->ws_route = moe::RouteWs::make(p->T, p->E).total;
   // forward transients: A [slot_cap, n], Y [slot_cap, d]
@@ -326,6 +354,22 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
   if (e_join == hipSuccess) e_join = hipStreamWaitEvent(sm, side->join, 0);
   if (e_main != hipSuccess || e_side != hipSuccess || e_join != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+int moe_gate_bwd(const moe_problem* p, const float* logits, const float* dS, const moe_routing* r,
+                 float* dlogits, void* stream, const moe_trace* trace) {
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(logits) || !aligned16(dS) || !routing_ok(r) || !aligned16(dlogits) ||
+      !trace_ok(trace))
+    return MOE_ERR_INVALID;
+  hipStream_t sm = static_cast<hipStream_t>(stream);
+  const moe::TraceHook tr = hook(trace);
+  tr.mark(sm, 0);
+  const hipError_t e = moe::launch_gate_bwd(logits, dS, r->token_offsets, r->token_slots,
+                                            r->expert_offsets, dlogits, int(p->T), int(p->E), sm);
+  tr.mark(sm, 1);
+  return hip_status(e);
 }
 
 int moe_router_fwd(const moe_problem* p, const void* X, const void* Wr, float* logits,

@@ -10,6 +10,7 @@
 // Decisions are taken in the precision the method states for them: top-K on
 // the fp32 logits (equal logits go to the lower expert), the token-rounding
 // order on fp64 softmax probabilities (equal keys go to the lower token).
+// Non-finite logits are first brought into the finite range (finite_logit).
 //
 // Kernels, in launch order on one stream:
 //   route_topk    per token: top-K, fp64 softmax keys for all experts, the
@@ -115,6 +116,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
   for (int j = 0; j < EPL; ++j)
     lv[j] = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(rrow, uint32_t(sub + kTopkLanes * j) * 4u, 0, 0));
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) lv[j] = finite_logit(lv[j]);
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = sub + kTopkLanes * j;

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kDlThreads) void k_router_dlogits(
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(e) * 4u, 0, 0));
+    x[j] = finite_logit(
+        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(e) * 4u, 0, 0)));
     g[w][e] = 0.0f;
   }
   __syncthreads();  // off[] staged (g is per wave)
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kDlThreads) void k_router_dlogits(
     const int e = lane + 64 * j;
     const float v = e < E ? p[j] * (g[w][e] - dot) : 0.0f;  // rows padded with zeros to Ep
     if (e < E) dlogits[int64_t(t) * E + e] = v;
-    dlp[int64_t(t) * Ep + e] = Elem<T>::store(v);
+    if (dlp) dlp[int64_t(t) * Ep + e] = Elem<T>::store(v);
   }
 }
 
@@ -326,6 +327,28 @@ hipError_t router_bwd_t(const RouterBwdArgs& a, hipStream_t st, const TraceHook&
                      dim3(256), 0, st, partials, static_cast<T*>(a.dWr), a.E, r.Ep, a.d,
                      r.nchunks);
   tr.mark(st, 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_bwd(const float* logits, const float* dS, const int32_t* token_offsets,
+                           const int32_t* token_slots, const int32_t* expert_offsets,
+                           float* dlogits, int Tn, int E, hipStream_t st) {
+  const int Ep = (E + 127) / 128 * 128;
+#define MOE_DLOGITS(EPL)                                                                      \
+  hipLaunchKernelGGL((k_router_dlogits<float, EPL>), dim3((Tn + 3) / 4), dim3(kDlThreads), 0, st, \
+                     logits, dS, token_offsets, token_slots, expert_offsets, dlogits,           \
+                     static_cast<float*>(nullptr), Tn, E, Ep)
+  switch (Ep / 64) {  // Ep is a multiple of 128, at most 1024
+    case 2: MOE_DLOGITS(2); break;
+    case 4: MOE_DLOGITS(4); break;
+    case 6: MOE_DLOGITS(6); break;
+    case 8: MOE_DLOGITS(8); break;
+    case 10: MOE_DLOGITS(10); break;
+    case 12: MOE_DLOGITS(12); break;
+    case 14: MOE_DLOGITS(14); break;
+    default: MOE_DLOGITS(16); break;
+  }
+#undef MOE_DLOGITS
   return hipGetLastError();
 }
 

@@ -14,36 +14,12 @@
 
 namespace moe {
 
-#ifndef MOE_TILE_VARIANT
-#define MOE_TILE_VARIANT 0
-#endif
-
-#if MOE_TILE_VARIANT == 1
-// 64-byte slabs: three stages for the 128 x 512 tiles, four for 256 x 256
-using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 3, 64, true>;
-using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 3, 64>;
-using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 4, 64>;
-using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
-#elif MOE_TILE_VARIANT == 2
-// as the default, with four stages of 64-byte slabs for the weight gradients
-using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
-using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
-using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 4, 64>;
-using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
-#elif MOE_TILE_VARIANT == 3
-// as the default, with four stages of 64-byte slabs for dH
-using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
-using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
-using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
-using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 4, 64>;
-#else
 // 128-byte slabs (one full cache line per row), two stages for the wide
 // tiles, three for dH (whose H reloads in the epilogue favour a deeper ring)
 using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
 using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
 using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
 using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
-#endif
 
 using DhWide512 = TileCfg<bf16_t, 64, 512, 1, 4, 2, 128>;  // dH for n = 512 (one wave per SIMD)
 using UpMid = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128, true>;

@@ -77,13 +77,14 @@ def lib():
     L.moe_fwd.argtypes = [P(Problem), V, V, V, P(RoutingStruct), V, V, V, S, V, P(Trace)]
     L.moe_bwd.argtypes = [P(Problem), V, V, V, V, V, P(RoutingStruct), V, V, V, V, V, S, V,
                           P(Trace)]
+    L.moe_gate_bwd.argtypes = [P(Problem), V, V, P(RoutingStruct), V, V, P(Trace)]
     L.moe_router_fwd.argtypes = [P(Problem), V, V, V, V, P(Trace)]
     L.moe_router_bwd.argtypes = [P(Problem), V, V, V, V, P(RoutingStruct), V, V, V, V, S, V,
                                  P(Trace)]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
-    for f in ("moe_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_router_fwd", "moe_router_bwd",
-              "moe_abi_version"):
+    for f in ("moe_sizes", "moe_route", "moe_fwd", "moe_bwd", "moe_gate_bwd", "moe_router_fwd",
+              "moe_router_bwd", "moe_abi_version"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -150,8 +151,11 @@ class Routing:
 
     @property
     def S(self) -> int:
-        """Slot count (copies one int from the device)."""
-        return int(self.tensors["totals"][0].item())
+        """Slot count.  The first read after moe_route copies one int from the
+        device (waiting for the routing); later reads reuse it."""
+        if self.__dict__.get("_S") is None:
+            self.__dict__["_S"] = int(self.tensors["totals"][0].item())
+        return self.__dict__["_S"]
 
 
 def alloc_routing(p: Problem, device="cuda") -> Routing:
@@ -192,6 +196,7 @@ def route(p: Problem, logits: torch.Tensor, rt: Routing | None = None, ws=None, 
             raise MoEError("stochastic token rounding needs round_rand ([E] draws)")
         rr = _dev(round_rand, "round_rand", torch.int32, (p.E,))
     rt = rt if rt is not None else alloc_routing(p, logits.device)
+    rt.__dict__["_S"] = None  # refilled below
     ws = ws if ws is not None else workspace(sizes(p).ws_route, logits.device)
     tr = _trace(events)
     _check(lib().moe_route(ctypes.byref(p), lg, rr, ctypes.byref(rt.struct),
@@ -200,8 +205,22 @@ def route(p: Problem, logits: torch.Tensor, rt: Routing | None = None, ws=None, 
     return rt
 
 
+def _h_arg(H, p: Problem, s: Sizes, rt: Routing, dt):
+    """H may have slot_cap rows, or fewer but at least S (checked against S
+    read back from the device, so that the kernels never write past it)."""
+    if not isinstance(H, torch.Tensor) or H.dim() != 2 or H.shape[1] != 2 * p.n:
+        raise MoEError(f"H must be [rows, {2 * p.n}]")
+    rows = H.shape[0]
+    if not 1 <= rows <= s.slot_cap:
+        raise MoEError(f"H must have between 1 and {s.slot_cap} rows, got {rows}")
+    if rows < s.slot_cap and rows < rt.S:
+        raise MoEError(f"H has {rows} rows, fewer than the {rt.S} slots of this routing")
+    return _dev(H, "H", dt)
+
+
 def forward(p: Problem, X, W1, W2, rt: Routing, out=None, ws=None, stream=None, events=None):
-    """moe_fwd: returns O [T, d] and H [slot_cap, 2n] (rows [0, S) valid)."""
+    """moe_fwd: returns O [T, d] and H [slot_cap, 2n] (rows [0, S) valid).
+    `out` = (O, H) may pass an H of fewer rows, down to S."""
     dt = torch_dtype(p)
     s = sizes(p)
     dev = X.device
@@ -213,7 +232,7 @@ def forward(p: Problem, X, W1, W2, rt: Routing, out=None, ws=None, stream=None, 
     ws = ws if ws is not None else workspace(s.ws_fwd, dev)
     tr = _trace(events)
     _check(lib().moe_fwd(ctypes.byref(p), x, w1, w2, ctypes.byref(rt.struct),
-                         _dev(O, "O", dt, (p.T, p.d)), _dev(H, "H", dt, (s.slot_cap, 2 * p.n)),
+                         _dev(O, "O", dt, (p.T, p.d)), _h_arg(H, p, s, rt, dt),
                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
                          ctypes.byref(tr) if tr else None))
     return O, H
@@ -234,7 +253,7 @@ def backward(p: Problem, dO, X, H, W1, W2, rt: Routing, out=None, ws=None, strea
     ws = ws if ws is not None else workspace(s.ws_bwd, dev)
     tr = _trace(events)
     _check(lib().moe_bwd(ctypes.byref(p), _dev(dO, "dO", dt, (p.T, p.d)),
-                         _dev(X, "X", dt, (p.T, p.d)), _dev(H, "H", dt, (s.slot_cap, 2 * p.n)),
+                         _dev(X, "X", dt, (p.T, p.d)), _h_arg(H, p, s, rt, dt),
                          _dev(W1, "W1", dt, (p.E, p.d, 2 * p.n)),
                          _dev(W2, "W2", dt, (p.E, p.n, p.d)), ctypes.byref(rt.struct),
                          _dev(dX, "dX", dt, (p.T, p.d)),
@@ -245,6 +264,21 @@ def backward(p: Problem, dO, X, H, W1, W2, rt: Routing, out=None, ws=None, strea
                          ctypes.byref(tr) if tr else None))
     return dX, dW1, dW2, dS
 
+
+
+def gate_backward(p: Problem, logits, dS, rt: Routing, out=None, stream=None,
+                  events=None) -> torch.Tensor:
+    """moe_gate_bwd: dlogits [T, E] fp32 from the slot gradients dS."""
+    s = sizes(p)
+    dl = out if out is not None else torch.empty(p.T, p.E, dtype=torch.float32,
+                                                 device=logits.device)
+    tr = _trace(events)
+    _check(lib().moe_gate_bwd(ctypes.byref(p), _dev(logits, "logits", torch.float32, (p.T, p.E)),
+                              _dev(dS, "dS", torch.float32, (s.slot_cap,)),
+                              ctypes.byref(rt.struct),
+                              _dev(dl, "dlogits", torch.float32, (p.T, p.E)), _stream(stream),
+                              ctypes.byref(tr) if tr else None))
+    return dl
 
 
 def router_forward(p: Problem, X, Wr, out=None, stream=None, events=None) -> torch.Tensor:
@@ -284,10 +318,16 @@ def router_backward(p: Problem, X, Wr, logits, dS, rt: Routing, dX, out=None, ws
 
 
 class MoELayerFunction(torch.autograd.Function):
-    """Autograd wrapper.  Saves exactly X and H (plus the routing metadata) for
-    the backward; the router-facing gradient dS is left on the routing object
-    (``routing.dS``) because the router itself sits outside this layer.  The
-    draws of stochastic rounding (``round_rand``) are an input."""
+    """Autograd op of the layer: X, W1, W2 and the router logits -> O.
+
+    It keeps for the backward exactly what the notes' key design 3 keeps: X,
+    H and the routing metadata (plus references to the weights, and to the
+    logits when they require a gradient).  H is allocated with exactly S
+    rows: after routing, the slot count is read back from the device (one
+    4-byte copy, which waits for the routing kernels).  The backward returns
+    dX, dW1, dW2 and, when the logits require a gradient, dlogits through
+    the gate's softmax backward (moe_gate_bwd).  The draws of stochastic
+    rounding (``round_rand``) are an input."""
 
     @staticmethod
     def forward(ctx, X, W1, W2, logits, K, M_tile, mode, round_rand):
@@ -295,18 +335,20 @@ class MoELayerFunction(torch.autograd.Function):
         E, _, n2 = W1.shape
         p = problem(T, d, n2 // 2, E, K, M_tile, X.dtype, mode)
         rt = route(p, logits, round_rand=round_rand)
-        O, H = forward(p, X, W1, W2, rt)
-        ctx.save_for_backward(X, H, W1, W2)
+        H = torch.empty(max(rt.S, 1), n2, dtype=X.dtype, device=X.device)
+        O, H = forward(p, X, W1, W2, rt, out=(torch.empty_like(X), H))
+        need_dl = ctx.needs_input_grad[3]
+        ctx.save_for_backward(X, H, W1, W2, logits if need_dl else None)
         ctx.moe = (p, rt)
         return O
 
     @staticmethod
     def backward(ctx, dO):
-        X, H, W1, W2 = ctx.saved_tensors
+        X, H, W1, W2, logits = ctx.saved_tensors
         p, rt = ctx.moe
         dX, dW1, dW2, dS = backward(p, dO.contiguous(), X, H, W1, W2, rt)
-        rt.tensors["dS"] = dS
-        return dX, dW1, dW2, None, None, None, None, None
+        dl = gate_backward(p, logits, dS, rt) if ctx.needs_input_grad[3] else None
+        return dX, dW1, dW2, dl, None, None, None, None
 
 
 def moe_layer(X, W1, W2, logits, K, M_tile, mode="tr", round_rand=None):
@@ -316,8 +358,9 @@ def moe_layer(X, W1, W2, logits, K, M_tile, mode="tr", round_rand=None):
 class MoERouterLayerFunction(torch.autograd.Function):
     """The whole layer with its router: logits = X Wr^T are computed by the
     library, and the backward returns dX (experts' and router's shares), dWr,
-    dW1 and dW2.  Saves X, H, Wr, W1, W2, the logits and the routing; the
-    draws of stochastic rounding (``round_rand``) are an input."""
+    dW1 and dW2.  Saves X, H (exactly S rows, as MoELayerFunction), Wr, W1,
+    W2, the logits and the routing; the draws of stochastic rounding
+    (``round_rand``) are an input."""
 
     @staticmethod
     def forward(ctx, X, Wr, W1, W2, K, M_tile, mode, round_rand):
@@ -326,7 +369,8 @@ class MoERouterLayerFunction(torch.autograd.Function):
         p = problem(T, d, n2 // 2, E, K, M_tile, X.dtype, mode)
         logits = router_forward(p, X, Wr)
         rt = route(p, logits, round_rand=round_rand)
-        O, H = forward(p, X, W1, W2, rt)
+        H = torch.empty(max(rt.S, 1), n2, dtype=X.dtype, device=X.device)
+        O, H = forward(p, X, W1, W2, rt, out=(torch.empty_like(X), H))
         ctx.save_for_backward(X, H, Wr, W1, W2, logits)
         ctx.moe = (p, rt)
         return O

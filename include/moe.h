@@ -21,7 +21,7 @@
  * dim d, expert intermediate dim n, E experts, K experts per token, and the
  * GEMM M tile M_tile that token rounding aligns counts to.
  *   X  [T, d]         W1 [E, d, 2n]  (columns [0, n) gate, [n, 2n) up)
- *   W2 [E, n, d]      O  [T, d]       H  [slot_cap, 2n]  (pre-activation)
+ *   W2 [E, n, d]      O  [T, d]       H  [>= S, 2n]  (pre-activation)
  * All matrices are dense, row-major, with no padding between rows.
  *
  * Conventions for every entry point:
@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Rows per M tile of the grouped GEMMs; the tile schedule in moe_routing is
  * expressed in these units. */
@@ -84,8 +84,16 @@ typedef struct {
   int32_t mode;  /* moe_route_mode */
 } moe_problem;
 
+/*
+ * slot_cap bounds the slot count S = sum of r_e of every routing of the
+ * problem, per mode: TC and TR_DOWN keep at most T*K pairs; TR pads an
+ * expert only when the upward gap is below M_tile/2, so by at most
+ * floor((M_tile-1)/2) slots; TR_UP and TR_STOCHASTIC pad by at most
+ * M_tile-1.  Hence slot_cap = min(T*K + E*pad, T*E) with pad = 0,
+ * floor((M_tile-1)/2) or M_tile-1.
+ */
 typedef struct {
-  int64_t slot_cap; /* upper bound on slots S: T*K + E*M_tile                  */
+  int64_t slot_cap; /* upper bound on slots S (see above)                      */
   int64_t tile_cap; /* upper bound on M tiles: ceil(slot_cap/TILE_M) + E       */
   size_t ws_route;  /* workspace bytes moe_route needs                         */
   size_t ws_fwd;    /* workspace bytes moe_fwd needs                           */
@@ -134,15 +142,25 @@ typedef struct {
  * Errors: MOE_ERR_INVALID for null arguments or T, d, n, E, K, M_tile < 1,
  * K > E, unknown dtype/mode; MOE_ERR_UNSUPPORTED for K > 32, E > 1024,
  * d % 128 != 0, n not in {64, 128, 256, 384, 512}, M_tile > 1024, sizes whose
- * slot or element counts overflow 32-bit indexing, or an X / dO / H / dH /
- * A / Y array (T x d, slot_cap x 2n, slot_cap x d) of more than 4 GiB - 1
- * bytes. */
+ * slot or element counts overflow 32-bit indexing, or an array that a kernel
+ * addresses through a 32-bit byte extent exceeding 4 GiB - 1 bytes: X, dO,
+ * O, dX (T x d); H, dH (slot_cap x 2n); Y, dX-tilde (slot_cap x d); one
+ * expert of W1 (d x 2n) or W2 (n x d); Wr (E x d); logits (T x E fp32); the
+ * router backward's padded copy of dlogits (T x ceil(E/128)*128).
+ * Why these limits: the tile shapes of this build cover d in multiples of
+ * 128 and the listed n (the GEMM tiles take whole 128-column slabs of d and
+ * whole gate/up halves of n); the routing kernels keep one token's experts
+ * and one expert's ranking state in a workgroup (K <= 32, E <= 1024). */
 int moe_sizes(const moe_problem *p, moe_sizes_t *out);
 
 /*
  * Routing (notes, key design 1).  logits: [T, E] fp32 device buffer.
  *   p[t,e]  = softmax over the E logits of token t, evaluated in fp64;
  *   TopK(t) = the K largest fp32 logits, equal logits to the lower expert;
+ *   non-finite logits count as finite ones first: NaN and -inf as -FLT_MAX,
+ *   +inf as +FLT_MAX (reading: the pages' router scores are real numbers;
+ *   this gives such inputs one ranking, a NaN below every number, and a
+ *   finite softmax);
  *   f_e     = number of tokens whose TopK holds e;
  *   TC:  r_e = f_e and expert e keeps exactly those tokens;
  *   TR*: lo/hi = the multiples of M_tile just below/above f_e, and r_e is
@@ -174,7 +192,10 @@ int moe_route(const moe_problem *p, const float *logits, const uint32_t *round_r
  *   A_e = SiLU(H_e[:, :n]) * H_e[:, n:]   (epilogue, from H rounded to dtype)
  *   Y_e = A_e W2_e
  *   O[t] = sum over t's slots of s * Y   (a token without slots gets 0)
- * Outputs: O [T, d]; H [slot_cap, 2n], rows [0, S) valid, saved for moe_bwd.
+ * Outputs: O [T, d]; H [rows, 2n] with rows >= S (slot_cap always suffices;
+ * a caller that has read S = totals[0] back may allocate exactly S rows),
+ * saved for moe_bwd.  Only rows [0, S) of H are written or, by moe_bwd,
+ * read; the library cannot check `rows` and a smaller H is overrun.
  * ws: at least sizes.ws_fwd bytes (holds the transient A and Y).
  */
 int moe_fwd(const moe_problem *p, const void *X, const void *W1,
@@ -190,6 +211,7 @@ int moe_fwd(const moe_problem *p, const void *X, const void *W1,
  *                           dA * SiLU(g)]  with g, u the halves of H
  *   dX[t] = sum over t's slots of dH W1_e^T
  *   dW1_e = X[I_e]^T dH_e,   dW2_e = (s * A_e)^T dO[I_e]   (varlen-K)
+ * H: as moe_fwd wrote it (at least S rows).
  * Outputs: dX [T, d], dW1 [E, d, 2n], dW2 [E, n, d] (experts without slots
  * get zeros), dS [slot_cap] fp32 with rows [0, S) valid.
  * ws: at least sizes.ws_bwd bytes.
@@ -206,6 +228,25 @@ int moe_bwd(const moe_problem *p, const void *dO, const void *X, const void *H,
             const void *W1, const void *W2, const moe_routing *r, void *dX,
             void *dW1, void *dW2, float *dS, void *ws, size_t ws_bytes,
             void *stream, const moe_trace *trace);
+
+/*
+ * Backward of the gate weights alone (notes, method > overall framework: the
+ * layer's backward yields the router gradients; dS is the layer's
+ * router-facing output).  With s = softmax(logits[t])[e] for every kept pair
+ * (no renormalisation) and g[t, e] = dS of the slot of (t, e), 0 where the
+ * pair is not kept (routing decisions carry no gradient):
+ *   dlogits[t] = p[t] * (g[t] - <p[t], g[t]>),  p = softmax(logits[t]) (fp32,
+ *                non-finite logits replaced as moe_route does)
+ * For callers whose router is not the linear map of moe_router_fwd: they
+ * take dlogits into their own router's backward.  Inputs: logits [T, E] fp32
+ * (those moe_route read), dS [slot_cap] fp32 from moe_bwd, `r` from
+ * moe_route.  Output: dlogits [T, E] fp32.  All device buffers, caller-owned,
+ * 16-byte aligned; no workspace; asynchronous on `stream`; a trace records 1
+ * kernel.  Errors as moe_sizes, MOE_ERR_INVALID for null or misaligned
+ * buffers.
+ */
+int moe_gate_bwd(const moe_problem *p, const float *logits, const float *dS,
+                 const moe_routing *r, float *dlogits, void *stream, const moe_trace *trace);
 
 /*
  * Router forward (notes, method > overall framework and key design 1: tokens

@@ -19,6 +19,9 @@ Readings where the pages are silent (each one is listed in the design doc):
   * gate = softmax over all E experts of the fp32 logits, computed in fp64;
     the top-K gate weights are NOT renormalised (s = p);
   * top-K ties go to the lower expert index (decided on the fp32 logits);
+  * non-finite logits are brought into the finite fp32 range before routing:
+    NaN and -inf become -FLT_MAX, +inf becomes +FLT_MAX (so a NaN ranks
+    below every number and gets probability 0 next to any larger logit);
   * token-rounding sort key = (chosen by token-choice?, p) descending, ties to
     the lower token index; the rounding tie (equal gaps) rounds DOWN, and a
     round-up that would need more than T tokens rounds down;
@@ -50,14 +53,29 @@ TR_MODES = (TR, TR_UP, TR_DOWN, TR_STOCHASTIC)
 # Routing
 # --------------------------------------------------------------------------
 
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def finite_logits(logits):
+    """The logits with non-finite entries replaced: NaN and -inf by -FLT_MAX,
+    +inf by +FLT_MAX (fp64 input keeps its precision, anything else is taken
+    as fp32).  Router scores are real numbers on the pages (notes, key design
+    1); this fixes one ranking and one gate for inputs outside that domain, so
+    that both routing sides agree on them."""
+    a = np.asarray(logits)
+    a = a if a.dtype == np.float64 else a.astype(np.float32)
+    return np.nan_to_num(a, nan=-FLT_MAX, posinf=FLT_MAX, neginf=-FLT_MAX)
+
+
 def softmax_probs(logits):
     """Router probabilities p[t, e] = softmax over experts of the logits, fp64.
 
     The abstract and the notes' framework section route every token by router
     scores; the gate is a softmax over all E experts (the plainest reading;
-    the pages do not print the gate formula).
+    the pages do not print the gate formula).  Non-finite logits are first
+    replaced as `finite_logits` states.
     """
-    z = np.asarray(logits, dtype=np.float64)
+    z = np.asarray(finite_logits(logits), dtype=np.float64)
     z = z - z.max(axis=1, keepdims=True)
     ez = np.exp(z)
     return ez / ez.sum(axis=1, keepdims=True)
@@ -68,9 +86,10 @@ def topk_token_choice(logits, K):
     largest logit, best first; equal logits go to the lower expert index.
 
     Softmax is monotone per row, so ranking the fp32 logits ranks p.
+    Non-finite logits are first replaced as `finite_logits` states.
     Returns int64 [T, K].
     """
-    l32 = np.asarray(logits, dtype=np.float32)
+    l32 = finite_logits(np.asarray(logits, dtype=np.float32))
     T, E = l32.shape
     if not 1 <= K <= E:
         raise ValueError("need 1 <= K <= E")

@@ -28,12 +28,12 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert names == ["moe_abi_version", "moe_bwd", "moe_fwd", "moe_route", "moe_router_bwd",
-                     "moe_router_fwd", "moe_sizes", "moe_status_string"]
+    assert names == ["moe_abi_version", "moe_bwd", "moe_fwd", "moe_gate_bwd", "moe_route",
+                     "moe_router_bwd", "moe_router_fwd", "moe_sizes", "moe_status_string"]
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 def test_status_strings():
@@ -46,12 +46,48 @@ def test_status_strings():
 def test_sizes_7b_layer():
     p = moe.problem(16384, 1536, 256, 128, 8, 128)
     s = moe.sizes(p)
-    assert s.slot_cap == 16384 * 8 + 128 * 128
+    assert s.slot_cap == 16384 * 8 + 128 * 63
     assert s.tile_cap == -(-s.slot_cap // 128) + 128
     esz = 2
     assert s.ws_fwd >= s.slot_cap * (256 + 1536) * esz
     assert s.ws_bwd >= s.slot_cap * (512 + 256 + 1536) * esz
     assert s.ws_route >= 16384 * 128 * 8
+
+
+@pytest.mark.parametrize("mode,pad", [("tc", 0), ("tr_down", 0), ("tr", 63), ("tr_up", 127),
+                                      ("tr_stochastic", 127)])
+def test_slot_cap_per_mode(mode, pad):
+    # token choice keeps T K pairs; nearest rounding pads an expert only when
+    # the upward gap is below M/2 (at most floor((M-1)/2) = 63 slots for
+    # M = 128), up and stochastic rounding by at most M - 1, down never
+    for T, d, n, E, K in ((16384, 1536, 256, 128, 8), (8192, 2048, 384, 512, 8)):
+        s = moe.sizes(moe.problem(T, d, n, E, K, 128, mode=mode))
+        assert s.slot_cap == T * K + E * pad
+    # odd M: nearest pads by at most (M - 1) / 2
+    s = moe.sizes(moe.problem(900, 256, 128, 12, 3, 49, mode="tr"))
+    assert s.slot_cap == 900 * 3 + 12 * 24
+    # no expert can hold more than T tokens: the bound is capped at T E
+    s = moe.sizes(moe.problem(1, 128, 64, 4, 2, 16, mode="tr_up"))
+    assert s.slot_cap == 4
+
+
+def test_slot_cap_bounds_every_rounding():
+    # brute force over every token-choice count vector of a small problem:
+    # the rounded total never exceeds the mode's slot_cap
+    import itertools
+
+    from oracle import moe_oracle as orc
+    T, E, K, M = 7, 3, 2, 4
+    u = [0, 1 << 31, (1 << 32) - 1]
+    for mode, cm in (("tc", orc.TC), ("tr", orc.TR), ("tr_up", orc.TR_UP),
+                     ("tr_down", orc.TR_DOWN), ("tr_stochastic", orc.TR_STOCHASTIC)):
+        cap = moe.sizes(moe.problem(T, 128, 64, E, K, M, mode=mode)).slot_cap
+        worst = 0
+        for f in itertools.product(range(T + 1), repeat=E):
+            if sum(f) != T * K:
+                continue
+            worst = max(worst, int(orc.round_counts(f, M, T, cm, u).sum()))
+        assert worst <= cap, (mode, worst, cap)
 
 
 def test_sizes_fp32_doubles_transients():
@@ -73,6 +109,31 @@ def test_invalid_problems(field, value, status):
     setattr(p, field, value)
     s = moe.Sizes()
     assert moe.lib().moe_sizes(ctypes.byref(p), ctypes.byref(s)) == status
+
+
+@pytest.mark.parametrize("dims,what", [
+    # one expert of W1 (d x 2n bf16) past 4 GiB: d = 2^22, n = 512
+    ((2, 1 << 22, 512, 2, 1, 16), "W1 expert"),
+    # the router's padded dlogits copy (T x ceil(E/128)*128 bf16) past 4 GiB,
+    # with every activation array below it: T = 2.2M, d = 128, n = 64,
+    # E = 1024, K = 1
+    ((2_200_000, 128, 64, 1024, 1, 16), "router dl copy"),
+    # logits (T x E fp32) past 4 GiB
+    ((1_100_000, 128, 64, 1024, 1, 16), "logits"),
+])
+def test_byte_extent_limits(dims, what):
+    p = moe.problem(*dims, mode="tc")
+    s = moe.Sizes()
+    assert moe.lib().moe_sizes(ctypes.byref(p), ctypes.byref(s)) == UNSUPPORTED, what
+
+
+def test_extent_limit_is_tight():
+    # just below the logits limit (T E 4 bytes <= 4 GiB - 1) the problem is
+    # accepted
+    T = (1 << 32) // (4 * 1024) - 1
+    p = moe.problem(T, 128, 64, 1024, 1, 16, mode="tc")
+    s = moe.Sizes()
+    assert moe.lib().moe_sizes(ctypes.byref(p), ctypes.byref(s)) == OK
 
 
 def _routing(ptr=FAKE):
@@ -138,6 +199,20 @@ def test_null_trace_event_rejected():
     tr = moe.Trace(ev, 7)
     assert L.moe_route(ctypes.byref(p), FAKE, None, ctypes.byref(_routing()), FAKE, need, None,
                        ctypes.byref(tr)) == INVALID
+
+
+def test_gate_bwd_validation_before_launch():
+    L = moe.lib()
+    p = moe.problem(256, 128, 64, 8, 2, 16)
+    rr = ctypes.byref(_routing())
+    assert L.moe_gate_bwd(ctypes.byref(p), None, FAKE, rr, FAKE, None, None) == INVALID
+    assert L.moe_gate_bwd(ctypes.byref(p), FAKE, FAKE + 4, rr, FAKE, None, None) == INVALID
+    assert L.moe_gate_bwd(ctypes.byref(p), FAKE, FAKE, ctypes.byref(_routing(0)), FAKE, None,
+                          None) == INVALID
+    assert L.moe_gate_bwd(ctypes.byref(p), FAKE, FAKE, rr, None, None, None) == INVALID
+    bad = moe.problem(256, 128, 64, 8, 2, 16)
+    bad.K = 9
+    assert L.moe_gate_bwd(ctypes.byref(bad), FAKE, FAKE, rr, FAKE, None, None) == INVALID
 
 
 def test_router_validation_before_launch():

@@ -253,3 +253,42 @@ def test_variants_with_m1_equal_tc(mode):
     tr = orc.route(logits, 3, 1, mode, np.zeros(9, np.uint64))
     assert np.array_equal(tc.slot_token, tr.slot_token)
     assert np.array_equal(tc.expert_offsets, tr.expert_offsets)
+
+
+def test_nonfinite_logits_rule_hand_worked():
+    # Hand-worked rows under the rule stated in the oracle (NaN and -inf rank
+    # as -FLT_MAX, +inf as +FLT_MAX; equal values to the lower expert):
+    #   row 0  [nan, 1, -inf, +inf, 0]  -> ranks e3 (+inf), e1 (1), e4 (0), ...
+    #          softmax: e3 holds all the mass, every other entry is exactly 0
+    #   row 1  [nan, nan, -inf, 0, 0]   -> e3, e4 (equal, lower first); the
+    #          three saturated entries underflow: p = (0, 0, 0, 1/2, 1/2)
+    #   row 2  [nan] * 5                -> all equal: e0, e1; p = 1/5 each
+    #   row 3  [-inf, +inf, +inf, 2, nan] -> e1, e2 (equal, lower first);
+    #          p = (0, 1/2, 1/2, 0, 0)
+    nan, inf = float("nan"), float("inf")
+    logits = np.array([[nan, 1.0, -inf, inf, 0.0],
+                       [nan, nan, -inf, 0.0, 0.0],
+                       [nan] * 5,
+                       [-inf, inf, inf, 2.0, nan]], dtype=np.float32)
+    top = orc.topk_token_choice(logits, 2)
+    assert top.tolist() == [[3, 1], [3, 4], [0, 1], [1, 2]]
+    p = orc.softmax_probs(logits)
+    want = np.array([[0, 0, 0, 1, 0], [0, 0, 0, 0.5, 0.5], [0.2] * 5, [0, 0.5, 0.5, 0, 0]])
+    assert np.array_equal(p, want)
+    # routing (TC, K = 2) keeps exactly those pairs with those gate weights
+    rt = orc.route(logits, K=2, M=2, mode=orc.TC)
+    pairs = sorted(zip(rt.slot_token.tolist(), rt.slot_expert.tolist(), rt.slot_weight.tolist()))
+    assert pairs == [(0, 1, 0.0), (0, 3, 1.0), (1, 3, 0.5), (1, 4, 0.5), (2, 0, 0.2), (2, 1, 0.2),
+                     (3, 1, 0.5), (3, 2, 0.5)]
+
+
+def test_nonfinite_logits_finite_rows_unchanged():
+    # the replacement leaves every finite value alone, so finite inputs route
+    # exactly as before
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((64, 8)).astype(np.float32)
+    logits[0, 0] = np.finfo(np.float32).max
+    logits[1, 1] = -np.finfo(np.float32).max
+    assert np.array_equal(orc.finite_logits(logits), logits)
+    for t in range(64):
+        assert list(orc.topk_token_choice(logits, 3)[t]) == brute_topk(logits[t], 3)
