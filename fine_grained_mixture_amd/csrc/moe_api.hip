@@ -11,6 +11,13 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+// Fixed device scratch for moe_route_noalloc: the routing workspace of
+// callers that cannot allocate.  One copy per device, for the life of the
+// process.  Host code never passes `scratch` itself to a kernel (on the host
+// the name is a stand-in, not a device address): each device's address is
+// looked up once with hipGetSymbolAddress, with that device current.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_ROUTE_BYTES];
+
 namespace {
 
 using moe::cdiv;
@@ -144,6 +151,30 @@ hipError_t side_stream(hipStream_t caller, SideStream** out) {
   return hipSuccess;
 }
 
+// The current device's copy of `scratch` is looked up once per device and
+// kept in g_scratch_ptr (see the definition of `scratch` above).
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use).
+hipError_t scratch_ptr(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 bool routing_ok(const moe_routing* r) {
   return r && aligned16(r->tc_counts) && aligned16(r->counts) && aligned16(r->expert_offsets) &&
          aligned16(r->expert_order) && aligned16(r->topk_ids) && aligned16(r->slot_token) &&
@@ -217,6 +248,23 @@ int moe_sizes(const moe_problem* p, moe_sizes_t* out) {
   if (!out) return MOE_ERR_INVALID;
   sizes_of(p, out);
   return MOE_OK;
+}
+
+int moe_route_noalloc(const moe_problem* p, const float* logits, const uint32_t* round_rand,
+                      const moe_routing* r, void* stream, const moe_trace* trace) {
+  // the same validation as moe_route, before any HIP call
+  int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aligned16(logits) || !routing_ok(r) || !trace_ok(trace)) return MOE_ERR_INVALID;
+  if (p->mode == MOE_ROUTE_TR_STOCHASTIC &&
+      (!round_rand || reinterpret_cast<uintptr_t>(round_rand) % 4 != 0))
+    return MOE_ERR_INVALID;
+  moe_sizes_t s;
+  sizes_of(p, &s);
+  if (s.ws_route > size_t(MOE_NOALLOC_ROUTE_BYTES)) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return moe_route(p, logits, round_rand, r, ws, s.ws_route, stream, trace);
 }
 
 int moe_route(const moe_problem* p, const float* logits, const uint32_t* round_rand,

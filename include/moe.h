@@ -186,6 +186,27 @@ int moe_route(const moe_problem *p, const float *logits, const uint32_t *round_r
               const moe_trace *trace);
 
 /*
+ * moe_route without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It computes exactly what moe_route computes, with
+ * the same arguments and errors, but its workspace is a fixed array in the
+ * library's device memory (one per GPU, MOE_NOALLOC_ROUTE_BYTES = 48 MiB,
+ * held until the process ends) instead of a caller buffer; it calls no
+ * allocator.  Problems whose sizes.ws_route exceeds MOE_NOALLOC_ROUTE_BYTES
+ * (E * T * 8 bytes of sort keys plus about 3%: E * T up to about 6.1M, e.g.
+ * T = 16384 tokens with E = 256, or T = 8192 with E = 512) return
+ * MOE_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that array: calls that overlap on one GPU (on different streams,
+ * or from different threads without ordering) race and must not be made.
+ * No part of the array needs to start at zero (each call writes every byte
+ * it reads).  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress; no allocation) with that device current.
+ */
+#define MOE_NOALLOC_ROUTE_BYTES (48 * 1024 * 1024)
+int moe_route_noalloc(const moe_problem *p, const float *logits, const uint32_t *round_rand,
+                      const moe_routing *r, void *stream, const moe_trace *trace);
+
+/*
  * Forward (notes, method > overall framework; key design 2).  For every
  * expert e with kept tokens I_e:
  *   H_e = X[I_e] W1_e          (rows gathered inside the GEMM operand load)

@@ -29,7 +29,8 @@ def declared_functions():
 def test_exports_every_declared_function():
     names = declared_functions()
     assert names == ["moe_abi_version", "moe_bwd", "moe_fwd", "moe_gate_bwd", "moe_route",
-                     "moe_router_bwd", "moe_router_fwd", "moe_sizes", "moe_status_string"]
+                     "moe_route_noalloc", "moe_router_bwd", "moe_router_fwd", "moe_sizes",
+                     "moe_status_string"]
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -230,3 +231,27 @@ def test_router_validation_before_launch():
                             FAKE, FAKE, s.ws_router, None, None) == INVALID
     assert L.moe_router_bwd(ctypes.byref(p), *args, rr, None, FAKE, FAKE, FAKE, s.ws_router,
                             None, None) == INVALID
+
+
+def test_route_noalloc_rejects_before_any_hip_call():
+    # the fixed scratch holds 48 MiB: a routing workspace beyond it is refused
+    # with MOE_ERR_WORKSPACE, and bad arguments as moe_route refuses them,
+    # all before the library touches the device
+    L = moe.lib()
+    L.moe_route_noalloc.argtypes = [ctypes.POINTER(moe.Problem), ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.POINTER(moe.RoutingStruct),
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    rr = ctypes.byref(_routing())
+    big = moe.problem(16384, 128, 64, 512, 2, 16)  # keys alone: 512 * 16384 * 8 = 64 MiB
+    assert moe.sizes(big).ws_route > 48 << 20
+    assert L.moe_route_noalloc(ctypes.byref(big), FAKE, None, rr, None, None) == WORKSPACE
+    p = moe.problem(16384, 1536, 256, 128, 8, 128)
+    assert moe.sizes(p).ws_route <= 48 << 20
+    assert L.moe_route_noalloc(ctypes.byref(p), None, None, rr, None, None) == INVALID
+    assert L.moe_route_noalloc(ctypes.byref(p), FAKE, None, ctypes.byref(_routing(0)), None,
+                               None) == INVALID
+    st = moe.problem(256, 128, 64, 8, 2, 16, mode="tr_stochastic")
+    assert L.moe_route_noalloc(ctypes.byref(st), FAKE, None, rr, None, None) == INVALID
+    bad = moe.problem(256, 128, 64, 8, 2, 16)
+    bad.K = 9
+    assert L.moe_route_noalloc(ctypes.byref(bad), FAKE, None, rr, None, None) == INVALID
