@@ -159,25 +159,78 @@ __device__ __forceinline__ float finite_logit(float x) {
   return x > kMax ? kMax : (x < -kMax ? -kMax : x);
 }
 
+// ---------------------------------------------------------------------------
+// Wave and workgroup prefix sums with DPP moves (no LDS round trip inside a
+// wave): shifts by 1, 2, 4 and 8 lanes inside each row of 16, then row 0's
+// and row 1's totals broadcast into the rows after them (row_bcast, gfx9).
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+  // lanes without a source (or outside ROW_MASK) get 0
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_or_zero<0x111>(v);        // row_shr:1
+  v += dpp_or_zero<0x112>(v);        // row_shr:2
+  v += dpp_or_zero<0x114>(v);        // row_shr:4
+  v += dpp_or_zero<0x118>(v);        // row_shr:8
+  v += dpp_or_zero<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's own LDS operations, not for its outstanding global loads and
+// stores (which __syncthreads would also drain), so loads issued earlier
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Exclusive prefix sum over the workgroup (at most 1024 threads, whole
+// waves); returns the exclusive prefix and writes the total to *total.
+// `sh` (LDS) needs one int per wave plus one.  Every thread must call it.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) sh[wave] = incl;
+  lds_barrier();
+  if (wave == 0) {
+    const int x = lane < nwaves ? sh[lane] : 0;
+    const int xi = wave_incl_scan(x);
+    if (lane < nwaves) sh[lane] = xi - x;
+    if (lane == nwaves - 1) sh[nwaves] = xi;
+  }
+  lds_barrier();
+  const int res = sh[wave] + incl - v;
+  *total = sh[nwaves];
+  lds_barrier();
+  return res;
+}
+
 // Routing workspace layout (byte offsets), shared by the host code and the
 // routing kernels.
 struct RouteWs {
   size_t keys;     // uint64 [E][T]  (is-token-choice << 63) | bits(p[t,e])
-  size_t bits_e;   // uint32 [E][nw] selection bitmap, expert-major (nw = ceil(T/32))
-  size_t bits_t;   // uint32 [T][W]  selection bitmap, token-major (W = ceil(E/32))
+  size_t bits_e;   // uint32 [E][nw] token-choice bitmap, expert-major (nw = ceil(T/32))
+  size_t bits_s;   // uint32 [E][nw] selection bitmap (the tokens each expert keeps)
   size_t wbase;    // int32  [E][nw] slots of expert e in words before w
-  size_t block_sum;  // int32 [E][ceil(T/256)] slots of expert e per block of 256 tokens
   size_t total;
   __host__ __device__ static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
   __host__ __device__ static RouteWs make(int64_t T, int64_t E) {
     RouteWs w;
-    const int64_t nw = (T + 31) / 32, W = (E + 31) / 32;
+    const int64_t nw = (T + 31) / 32;
     size_t o = 0;
     w.keys = o;   o = align(o + size_t(E) * T * 8);
     w.bits_e = o; o = align(o + size_t(E) * nw * 4);
-    w.bits_t = o; o = align(o + size_t(T) * W * 4);
+    w.bits_s = o; o = align(o + size_t(E) * nw * 4);
     w.wbase = o;  o = align(o + size_t(E) * nw * 4);
-    w.block_sum = o; o = align(o + size_t(E) * ((T + 255) / 256) * 4);
     w.total = o;
     return w;
   }

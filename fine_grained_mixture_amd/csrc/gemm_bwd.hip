@@ -256,32 +256,6 @@ __device__ __forceinline__ bool varlen_item(int b, int PT, const int* n_items,
 // kc2).  Thread q handles expert rank q (E <= 1024).
 constexpr int kPlanThreads = 1024;
 
-__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(x, o, 64);
-    if (lane >= o) x += u;
-  }
-  if (lane == 63) sh[wv] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      const int t = sh[w];
-      sh[w] = run;
-      run += t;
-    }
-    sh[kPlanThreads / 64] = run;
-  }
-  __syncthreads();
-  const int r = sh[wv] + x - v;
-  *total = sh[kPlanThreads / 64];
-  __syncthreads();
-  return r;
-}
-
 __device__ __forceinline__ void plan_one(const int32_t* offsets, const int32_t* order, int E,
                                          int kc, int* header, VarlenItem* items,
                                          VarlenSplit* splits, int* sh) {

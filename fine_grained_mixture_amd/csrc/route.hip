@@ -14,14 +14,13 @@
 //
 // Kernels, in launch order on one stream:
 //   route_topk    per token: top-K, fp64 softmax keys for all experts, the
-//                 token-choice bitmap (expert-major); clears the token-major
-//                 bitmap rows of its tokens
+//                 token-choice bitmap (expert-major)
 //   route_count   per expert: f_e = popcount of its bitmap row, r_e
 //   route_select  per expert: token-rounding threshold (radix select on the
 //                 64-bit keys), slot list in token order, gate weights, and
-//                 the expert's slots added to per-256-token block counts; one
-//                 extra workgroup scans the counts: expert offsets, the
-//                 M-tile schedule, the expert order by count, the totals
+//                 the expert's slots before each bitmap word; one extra
+//                 workgroup scans the counts: expert offsets, the M-tile
+//                 schedule, the expert order by count, the totals
 //   route_tslots  per token: CSR offset and its slots in ascending expert order
 #include "moe.h"
 #include "common.hpp"
@@ -32,34 +31,61 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
+// All-reduce across each row of 16 lanes with DPP moves (register
+// crossbar, no LDS round trip): swap neighbours, swap pairs, mirror inside
+// 8 lanes, mirror inside 16 lanes.  After each step every lane combines its
+// value with one lane of the other half of a growing group, so after the
+// four steps all 16 lanes hold the reduction of the row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return uint64_t(dpp32<CTRL>(uint32_t(v))) | (uint64_t(dpp32<CTRL>(uint32_t(v >> 32))) << 32);
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i inside 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15 - i inside 16
+
+// AND and OR of a 64-bit value over the 64 lanes of a wave, valid in lane
+// 63: an all-reduce inside each row of 16, then rows 0-2 carried into the
+// rows after them with row broadcasts (disabled rows contribute the identity).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp32_or(uint32_t v, uint32_t ident) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(ident), int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void and_or_step(uint64_t& a, uint64_t& o) {
+  a &= uint64_t(dpp32_or<CTRL, ROW_MASK>(uint32_t(a), ~0u)) |
+       (uint64_t(dpp32_or<CTRL, ROW_MASK>(uint32_t(a >> 32), ~0u)) << 32);
+  o |= uint64_t(dpp32_or<CTRL, ROW_MASK>(uint32_t(o), 0u)) |
+       (uint64_t(dpp32_or<CTRL, ROW_MASK>(uint32_t(o >> 32), 0u)) << 32);
+}
+__device__ __forceinline__ void wave_and_or(uint64_t& a, uint64_t& o) {
+  and_or_step<0xB1>(a, o);         // quad_perm [1, 0, 3, 2]
+  and_or_step<0x4E>(a, o);         // quad_perm [2, 3, 0, 1]
+  and_or_step<0x141>(a, o);        // half mirror
+  and_or_step<0x140>(a, o);        // mirror: every lane holds its row's result
+  and_or_step<0x142, 0xA>(a, o);   // row_bcast:15 into rows 1 and 3
+  and_or_step<0x143, 0xC>(a, o);   // row_bcast:31 into rows 2 and 3
 }
 
-// Exclusive scan over the block; returns the exclusive prefix and writes the
-// block total to *total.  `sh` needs one int per wave plus one.
-__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  int incl = wave_incl_scan(v);
-  if (lane == 63) sh[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < nwaves; ++i) { int x = sh[i]; sh[i] = run; run += x; }
-    sh[nwaves] = run;
-  }
-  __syncthreads();
-  int res = sh[wave] + incl - v;
-  *total = sh[nwaves];
-  __syncthreads();
-  return res;
+__device__ __forceinline__ uint64_t row16_max(uint64_t v) {
+  uint64_t o;
+  o = dpp64<kDppXor1>(v); v = o > v ? o : v;
+  o = dpp64<kDppXor2>(v); v = o > v ? o : v;
+  o = dpp64<kDppHalfMirror>(v); v = o > v ? o : v;
+  o = dpp64<kDppMirror>(v); v = o > v ? o : v;
+  return v;
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v += __longlong_as_double(int64_t(dpp64<kDppXor1>(uint64_t(__double_as_longlong(v)))));
+  v += __longlong_as_double(int64_t(dpp64<kDppXor2>(uint64_t(__double_as_longlong(v)))));
+  v += __longlong_as_double(int64_t(dpp64<kDppHalfMirror>(uint64_t(__double_as_longlong(v)))));
+  v += __longlong_as_double(int64_t(dpp64<kDppMirror>(uint64_t(__double_as_longlong(v)))));
+  return v;
 }
 
 // Orders fp32 values as unsigned integers (larger float -> larger integer).
@@ -88,34 +114,31 @@ template <int EPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk(
     const float* __restrict__ logits, int T, int E, int K,
     int32_t* __restrict__ topk_ids,
-    uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e, uint32_t* __restrict__ bits_t) {
+    uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e) {
   static_assert(EPL >= 1 && EPL <= 64, "experts per lane");
   __shared__ uint32_t sbits[1024];
   __shared__ uint64_t stage[kStageE][kTopkTokens + 1];
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kTopkThreads) sbits[i] = 0u;
-  {
-    // this block's rows of the token-major bitmap start empty
-    const int W = (E + 31) >> 5;
-    const int64_t beg = int64_t(blockIdx.x) * kTopkTokens * W;
-    const int64_t end = min(int64_t(T), int64_t(blockIdx.x + 1) * kTopkTokens) * W;
-    for (int64_t i = beg + tid; i < end; i += kTopkThreads) bits_t[i] = 0u;
-  }
   __syncthreads();
 
   const int sub = tid & (kTopkLanes - 1), tl = tid / kTopkLanes;
   const int t = blockIdx.x * kTopkTokens + tl;
   const bool valid = t < T;
-  // the token's logits through a buffer descriptor over its row: positions
-  // past E read 0 (and are masked), so all EPL loads are issued together
-  const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(logits + int64_t(valid ? t : 0) * E), 0, E * 4, 0x00020000);
+  // the token's logits through one (wave-uniform) buffer descriptor over the
+  // whole array, T E 4 bytes (below 4 GiB, checked on the host): positions
+  // past E read the next row or, past the end, 0, and are masked below; all
+  // EPL loads are issued together
+  const __amdgpu_buffer_rsrc_t rlog = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(logits), 0, int(uint32_t(T) * uint32_t(E) * 4u), 0x00020000);
+  const uint32_t rowb = uint32_t(valid ? t : T - 1) * uint32_t(E) * 4u;
   float lv[EPL];     // this lane's logits
   uint32_t ok[EPL];  // ordered logits of this lane's experts (0: none)
 #pragma unroll
   for (int j = 0; j < EPL; ++j)
     lv[j] = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rrow, uint32_t(sub + kTopkLanes * j) * 4u, 0, 0));
+        float, __builtin_amdgcn_raw_buffer_load_b32(rlog, rowb + uint32_t(sub + kTopkLanes * j) * 4u,
+                                                    0, 0));
 #pragma unroll
   for (int j = 0; j < EPL; ++j) lv[j] = finite_logit(lv[j]);
 #pragma unroll
@@ -134,11 +157,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
                                                  : ((uint64_t(ok[j]) << 32) | (0xffffffffu - e));
       best = key > best ? key : best;
     }
-#pragma unroll
-    for (int o = 1; o < kTopkLanes; o <<= 1) {
-      const uint64_t other = __shfl_xor(best, o, 64);
-      best = other > best ? other : best;
-    }
+    best = row16_max(best);
     const int eb = int(0xffffffffu - uint32_t(best));
     if (k == 0) m = double(unordered_f32(uint32_t(best >> 32)));
     if ((eb & (kTopkLanes - 1)) == sub) taken |= 1ull << (eb / kTopkLanes);
@@ -157,8 +176,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
     ex[j] = (valid && e < E) ? exp(double(lv[j]) - m) : 0.0;
     z += ex[j];
   }
-#pragma unroll
-  for (int o = 1; o < kTopkLanes; o <<= 1) z += __shfl_xor(z, o, 64);
+  z = row16_sum(z);
   const double rz = 1.0 / z;
   __syncthreads();  // sbits complete; stage below reuses nothing of it
   // Keys go out expert-major (row e holds all T tokens): staged in LDS per
@@ -270,23 +288,22 @@ __device__ __forceinline__ void scan_body(int r, int E, int* sh, int* sr,
 // equal keys to the lower token, then list them in token order as slots.
 //
 // With KPT > 0 each of the 1024 threads holds the keys of tokens
-// t = j * 1024 + tid (j < KPT) in registers, so the eight 8-bit radix passes
-// need no memory traffic; KPT == 0 reads the keys from memory in every pass
-// (any T).
+// t = j * 1024 + tid (j < KPT) in registers, so the 8-bit radix passes need
+// no memory traffic; KPT == 0 reads the keys from memory in every pass (any
+// T).
 constexpr int kSelThreads = 1024;
 // at most this many keys left under the prefix: rank them directly
 constexpr int kSelFinish = 256;
 
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void route_select(
-    int T, int E, const int32_t* __restrict__ tc_counts,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ expert_offsets,
+    int T, int E, const int32_t* __restrict__ tc_counts, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ expert_order, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ tile_row, int32_t* __restrict__ totals,
-    const uint64_t* __restrict__ keys, uint32_t* __restrict__ bits_e,
-    uint32_t* __restrict__ bits_t, int32_t* __restrict__ wbase,
-    int32_t* __restrict__ slot_token, float* __restrict__ slot_weight,
-    int32_t* __restrict__ block_sum) {
+    const uint64_t* __restrict__ keys, const uint32_t* __restrict__ bits_e,
+    uint32_t* __restrict__ bits_s, int32_t* __restrict__ wbase, int32_t* __restrict__ slot_token,
+    float* __restrict__ slot_weight) {
   // 16 copies of the 256-bin histogram; the +1 pad puts the copies of one
   // digit in 16 different banks
   __shared__ uint32_t hist[16][257];
@@ -297,64 +314,125 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
   __shared__ int s_ncand;
   __shared__ uint64_t s_thr;
   __shared__ __attribute__((aligned(16))) int sr[1024];
+  // the expert's selection bitmap while it is built (T <= 32 K tokens; with
+  // more, the row of bits_s in global memory serves)
+  __shared__ uint32_t s_sel[KPT > 0 ? KPT * kSelThreads / 32 : 1];
+  // the kept tokens in slot order (T <= 32 K: 16-bit token ids), so that the
+  // gate weights are read in one parallel pass without a global barrier
+  __shared__ uint16_t s_list[KPT > 0 ? KPT * kSelThreads : 1];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int nw = (T + 31) >> 5;
+  // this thread's expert's count (its load issued before the keys', so the
+  // offset scan below does not wait for them)
+  const int my_r = tid < E ? counts[tid] : 0;
   if (e == E) {
     // the extra workgroup: offsets, tile schedule, expert order and totals
-    scan_body(tid < E ? counts[tid] : 0, E, sh, sr, expert_offsets, expert_order, tile_expert,
-              tile_row, totals);
+    scan_body(my_r, E, sh, sr, expert_offsets, expert_order, tile_expert, tile_row, totals);
     return;
   }
-  // this expert's first slot: the counts of the experts before it
-  int off;
-  {
-    int before;
-    block_excl_scan(tid < e ? counts[tid] : 0, sh, &before);
-    off = before;
-  }
   const int f = tc_counts[e], r = counts[e];
-  const int nw = (T + 31) >> 5;
-  const int W = (E + 31) >> 5;
   const uint64_t* ke = keys + int64_t(e) * T;
-  uint32_t* be = bits_e + int64_t(e) * nw;
-
-  if (r != f) {
-    uint64_t kr[KPT > 0 ? KPT : 1];
-    if constexpr (KPT > 0) {
+  // The keys of this expert, when rounding moved its count: issued now, so
+  // that their latency hides behind the offset scan (whose barriers wait for
+  // LDS only).
+  uint64_t kr[KPT > 0 ? KPT : 1];
+  if constexpr (KPT > 0) {
+    if (r != f) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int t = j * kSelThreads + tid;
         kr[j] = t < T ? ke[t] : 0ull;  // 0 ranks below every real key
       }
     }
-    uint64_t prefix = 0ull, mask = 0ull;
-    int rem = r;  // rank (from the top, 1-based) still to locate under prefix
-    int cnt_eq = 0;
+  }
+  // this expert's first slot: the counts of the experts before it
+  int off;
+  {
+    int before;
+    block_excl_scan(tid < e ? my_r : 0, sh, &before);
+    off = before;
+  }
+  // this expert's row of the selection bitmap: built in LDS when the keys
+  // sit in registers, else directly in bits_s (the token-choice bitmap is
+  // read by every workgroup's count above and is left as it is)
+  uint32_t* be = bits_s + int64_t(e) * nw;
+  uint32_t* sel = KPT > 0 ? s_sel : be;
+  auto sel_sync = [&] {
+    if constexpr (KPT > 0) lds_barrier();
+    else __syncthreads();
+  };
+
+  if (r == f) {
+    // the expert keeps exactly its token-choice tokens
+    const uint32_t* tc = bits_e + int64_t(e) * nw;
+    for (int w = tid; w < nw; w += kSelThreads) sel[w] = tc[w];
+    sel_sync();
+  } else {
+    // The r-th largest key lies in one class: among the tokens outside token
+    // choice when padding (every token-choice key ranks above them, so it is
+    // the (r - f)-th largest of that class), among the token-choice tokens
+    // when dropping.  The bits that every key of that class shares (the
+    // class bit, usually the top exponent bits too) are fixed first from the
+    // AND and OR of the class's keys, so the radix passes start at the
+    // highest bit where the class's keys differ.
+    const uint64_t cls = r > f ? 0ull : (1ull << 63);
+    uint64_t prefix = cls, mask = 1ull << 63;
+    int rem = r > f ? r - f : r;  // rank (from the top, 1-based) still to locate under prefix
+    int cnt_eq = r > f ? T - f : f;
+    int hi = -1;  // highest bit still undecided
     if (r > 0) {
-      for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
+      uint64_t a_and = ~0ull, a_or = 0ull;
+      if constexpr (KPT > 0) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const int t = j * kSelThreads + tid;
+          if (t < T && (kr[j] & mask) == prefix) { a_and &= kr[j]; a_or |= kr[j]; }
+        }
+      } else {
+        for (int t = tid; t < T; t += kSelThreads) {
+          const uint64_t k = ke[t];
+          if ((k & mask) == prefix) { a_and &= k; a_or |= k; }
+        }
+      }
+      wave_and_or(a_and, a_or);  // lane 63 holds the wave's AND and OR
+      if (lane == 63) { cand[2 * (tid >> 6)] = a_and; cand[2 * (tid >> 6) + 1] = a_or; }
+      lds_barrier();
+      a_and = ~0ull;
+      a_or = 0ull;
+      for (int w = 0; w < kSelThreads / 64; ++w) { a_and &= cand[2 * w]; a_or |= cand[2 * w + 1]; }
+      lds_barrier();  // cand is reused below
+      const uint64_t diff = (a_and ^ a_or) & ~mask;
+      hi = diff ? 63 - __clzll(diff) : -1;
+      const uint64_t common = hi >= 0 ? ~((2ull << hi) - 1) : ~0ull;  // bits above hi
+      prefix = (a_and & common) | cls;
+      mask = common;
+      while (hi >= 0) {
+        const int shift = hi >= 7 ? hi - 7 : 0;
+        const int nbits = hi - shift + 1;
+        const uint64_t dmask = (1ull << nbits) - 1;
         for (int i = tid; i < 16 * 257; i += kSelThreads) (&hist[0][0])[i] = 0u;
-        __syncthreads();
+        lds_barrier();
         uint32_t* hc = hist[tid & 15];
         if constexpr (KPT > 0) {
 #pragma unroll
           for (int j = 0; j < KPT; ++j) {
             const int t = j * kSelThreads + tid;
-            if (t < T && (kr[j] & mask) == prefix) atomicAdd(&hc[(kr[j] >> shift) & 255u], 1u);
+            if (t < T && (kr[j] & mask) == prefix) atomicAdd(&hc[(kr[j] >> shift) & dmask], 1u);
           }
         } else {
           for (int t = tid; t < T; t += kSelThreads) {
             const uint64_t k = ke[t];
-            if ((k & mask) == prefix) atomicAdd(&hc[(k >> shift) & 255u], 1u);
+            if ((k & mask) == prefix) atomicAdd(&hc[(k >> shift) & dmask], 1u);
           }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < 256) {
           uint32_t c = 0;
 #pragma unroll
           for (int q = 0; q < 16; ++q) c += hist[q][tid];
           tot[tid] = c;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < 64) {
           // lane l covers digits 255-4l .. 252-4l (descending)
           uint32_t c[4];
@@ -376,18 +454,19 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
             }
           }
         }
-        __syncthreads();
+        lds_barrier();
         prefix |= uint64_t(uint32_t(s_digit_info[0])) << shift;
-        mask |= 0xffull << shift;
+        mask |= dmask << shift;
         rem = s_digit_info[1];
         cnt_eq = s_digit_info[2];
-        __syncthreads();
-        if (KPT > 0 && pass < 7 && cnt_eq <= kSelFinish) {
+        hi = shift - 1;
+        lds_barrier();
+        if (KPT > 0 && hi >= 0 && cnt_eq <= kSelFinish) {
           // Few keys left under the prefix: gather them and find the rem-th
           // largest directly, by counting for each candidate the candidates
           // above it (and equal to it).
           if (tid == 0) s_ncand = 0;
-          __syncthreads();
+          lds_barrier();
           if constexpr (KPT > 0) {
 #pragma unroll
             for (int j = 0; j < KPT; ++j) {
@@ -395,28 +474,37 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
               if (t < T && (kr[j] & mask) == prefix) cand[atomicAdd(&s_ncand, 1)] = kr[j];
             }
           }
-          __syncthreads();
+          lds_barrier();
           const int nc = s_ncand;
-          if (tid < nc) {
-            const uint64_t mine = cand[tid];
+          {
+            // four threads per candidate (a lane quad), each comparing it
+            // with a quarter of the candidates; the quad adds its counts
+            const int ci = tid >> 2, qt = tid & 3;
+            const uint64_t mine = ci < nc ? cand[ci] : 0ull;
             int gt = 0, ge = 0;
-            for (int i = 0; i < nc; ++i) {
-              const uint64_t o = cand[i];
-              gt += o > mine;
-              ge += o >= mine;
-            }
-            if (gt < rem && rem <= ge) {  // every holder of this key writes the same
+            if (ci < nc)
+              for (int i = qt; i < nc; i += 4) {
+                const uint64_t o = cand[i];
+                gt += o > mine;
+                ge += o >= mine;
+              }
+            gt += dpp_or_zero<0xB1>(gt);  // quad_perm [1, 0, 3, 2]
+            gt += dpp_or_zero<0x4E>(gt);  // quad_perm [2, 3, 0, 1]
+            ge += dpp_or_zero<0xB1>(ge);
+            ge += dpp_or_zero<0x4E>(ge);
+            if (ci < nc && qt == 0 && gt < rem && rem <= ge) {
+              // every holder of this key writes the same
               s_thr = mine;
               s_digit_info[1] = rem - gt;
               s_digit_info[2] = ge - gt;
             }
           }
-          __syncthreads();
+          lds_barrier();
           prefix = s_thr;
           mask = ~0ull;
           rem = s_digit_info[1];
           cnt_eq = s_digit_info[2];
-          __syncthreads();
+          lds_barrier();
           break;
         }
       }
@@ -432,8 +520,8 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
         const bool keep = r > 0 && t < T && (kr[j] > prefix || (all_eq && kr[j] == prefix));
         const uint64_t m = __ballot(keep);
         const int w0 = t >> 5;  // even: lane 0 starts a word
-        if (lane == 0 && w0 < nw) be[w0] = uint32_t(m);
-        if (lane == 32 && w0 < nw) be[w0] = uint32_t(m >> 32);
+        if (lane == 0 && w0 < nw) sel[w0] = uint32_t(m);
+        if (lane == 32 && w0 < nw) sel[w0] = uint32_t(m >> 32);
       }
     } else {
       for (int w = tid; w < nw; w += kSelThreads) {
@@ -447,10 +535,10 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
             }
           }
         }
-        be[w] = word;
+        sel[w] = word;
       }
     }
-    __syncthreads();
+    sel_sync();
     if (r > 0 && !all_eq) {
       // several tokens share the boundary key: keep the lowest `rem` of them
       int taken = 0;
@@ -459,119 +547,121 @@ __global__ __launch_bounds__(kSelThreads) void route_select(
         const int flag = (t < T) && (ke[t] == prefix);
         int chunk;
         const int ex = block_excl_scan(flag, sh, &chunk);
-        if (flag && taken + ex < rem) atomicOr(&be[t >> 5], 1u << (t & 31));
+        if (flag && taken + ex < rem) atomicOr(&sel[t >> 5], 1u << (t & 31));
         taken += chunk;
       }
-      __syncthreads();
+      sel_sync();
     }
   }
 
-  // Compaction in token order: the word pass lists the kept tokens; a flat
-  // pass over the expert's slots then fetches all gate weights in parallel.
+  // Compaction in token order: each thread lists the kept tokens of one
+  // bitmap word as slots and records the slots before its word; the row of
+  // the selection bitmap goes out for the token CSR.  The gate weights then
+  // come from a flat pass over the slots, all loads in flight together.
   int carry = 0;
   for (int base = 0; base < nw; base += kSelThreads) {
     const int w = base + tid;
-    const uint32_t word = (w < nw) ? be[w] : 0u;
+    const uint32_t word = (w < nw) ? sel[w] : 0u;
     int chunk;
     const int ex = block_excl_scan(__popc(word), sh, &chunk);
-    int written = 0;
     if (w < nw) {
       const int wb = carry + ex;
       wbase[int64_t(e) * nw + w] = wb;
+      if constexpr (KPT > 0) be[w] = word;
       uint32_t m = word;
       int i = 0;
       // never past the expert's own r_e slots, whatever the bitmap holds
       while (m && wb + i < r) {
         const int b = __ffs(m) - 1;
         m &= m - 1;
-        slot_token[off + wb + i++] = w * 32 + b;
+        const int t = w * 32 + b;
+        slot_token[off + wb + i] = t;
+        if constexpr (KPT > 0) s_list[wb + i] = uint16_t(t);
+        ++i;
       }
-      written = i;
     }
-    // this expert's slots in each block of 256 tokens (8 words, 8
-    // consecutive lanes), for the token CSR
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) written += __shfl_xor(written, o, 64);
-    if ((lane & 7) == 0 && w < nw) block_sum[int64_t(e) * ((nw + 7) >> 3) + (w >> 3)] = written;
     carry += chunk;
   }
-  __syncthreads();
   const int kept = min(carry, r);
+  if constexpr (KPT > 0) lds_barrier();
+  else __syncthreads();
 #pragma unroll 4
   for (int i = tid; i < kept; i += kSelThreads) {
-    const int t = slot_token[off + i];
+    const int t = KPT > 0 ? int(s_list[i]) : slot_token[off + i];
     const uint64_t k = ke[t] & 0x7fffffffffffffffull;
     slot_weight[off + i] = float(__longlong_as_double(int64_t(k)));
-    atomicOr(&bits_t[int64_t(t) * W + (e >> 5)], 1u << (e & 31));
   }
 }
 
-// Per token: CSR offset (earlier blocks' slots, summed over the experts'
-// per-block counts, + exclusive scan inside the block) and the token's slots
-// in ascending expert order.
+// Per token: CSR offset and the token's slots in ascending expert order,
+// from the expert-major selection bitmap.  A block covers 64 tokens (2 bitmap
+// words) with 4 threads per token, each walking a contiguous quarter of the
+// experts.  It stages, per expert, its slot offset and, for both words, the
+// expert's slots before the word (wbase) and the word itself (word-major, so
+// that four experts' words are one 16-byte read).  The slots of every token
+// before the block are the sum over experts of wbase at the block's first
+// word; an exclusive scan over (token, quarter) in thread order then gives
+// every thread the position of its first slot.
+constexpr int kCsrTokens = 64;
 __global__ __launch_bounds__(256) void route_tslots(
-    int T, int E, const uint32_t* __restrict__ bits_t, const uint32_t* __restrict__ bits_e,
-    const int32_t* __restrict__ wbase, const int32_t* __restrict__ expert_offsets,
-    const int32_t* __restrict__ block_sum, int32_t* __restrict__ token_offsets,
+    int T, int E, const uint32_t* __restrict__ bits_s, const int32_t* __restrict__ wbase,
+    const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_offsets,
     int32_t* __restrict__ token_slots) {
-  // LDS: expert offsets [E]; wbase and bits_e of this block's 8 token words
-  // [E][8] each; the block's rows of the token-major bitmap [256][W]
+  // LDS: expert offsets [E4]; wbase and bits_s of this block's 2 token
+  // words, [2][E4] each (E padded to a multiple of 128 with empty experts)
   extern __shared__ int32_t dyn[];
+  const int E4 = (E + 127) & ~127;
   int32_t* s_off = dyn;
-  int32_t* s_wb = s_off + E;
-  uint32_t* s_be = reinterpret_cast<uint32_t*>(s_wb + E * 8);
-  uint32_t* s_bt = s_be + E * 8;
+  int32_t* s_wb = s_off + E4;
+  uint32_t* s_be = reinterpret_cast<uint32_t*>(s_wb + 2 * E4);
   __shared__ int sh[256 / 64 + 1];
-  const int W = (E + 31) >> 5, nw = (T + 31) >> 5, nblk = (nw + 7) >> 3;
-  const int tid = threadIdx.x, t0 = blockIdx.x * 256, t = t0 + tid, tw0 = blockIdx.x * 8;
-  // stage the lookups of this block's tokens (coalesced), so that the slot
-  // loop below reads LDS only
-  for (int i = tid; i < E; i += 256) s_off[i] = expert_offsets[i];
-  for (int i = tid; i < E * 8; i += 256) {
-    const int e = i >> 3, tw = tw0 + (i & 7);
-    s_wb[i] = tw < nw ? wbase[int64_t(e) * nw + tw] : 0;
-    s_be[i] = tw < nw ? bits_e[int64_t(e) * nw + tw] : 0u;
-  }
-  const int nrow = min(256, T - t0);
-  for (int i = tid; i < nrow * W; i += 256) s_bt[i] = bits_t[int64_t(t0) * W + i];
-  // slots of all earlier blocks: the entries [e][b] with b < this block, read
-  // in batches of 8 per thread through a buffer descriptor (positions past
-  // the count get an offset past the end and read 0, so no load waits behind
-  // a branch)
-  const int nb = blockIdx.x, n = E * nb;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(block_sum), 0, E * nblk * 4, 0x00020000);
+  const int nw = (T + 31) >> 5;
+  const int tid = threadIdx.x, tl = tid >> 2, sub = tid & 3;
+  const int t = blockIdx.x * kCsrTokens + tl, tw0 = blockIdx.x * 2;
   int before = 0;
-  for (int i0 = 0; i0 < n; i0 += 256 * 8) {
-    int v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * 256 + tid;
-      const uint32_t off = i < n ? uint32_t((i / nb) * nblk + i % nb) * 4u : 0xfffffff0u;
-      v[u] = int(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) before += v[u];
+  for (int i = tid; i < E4; i += 256) s_off[i] = i < E ? expert_offsets[i] : 0;
+  for (int i = tid; i < E4 * 2; i += 256) {
+    const int e = i >> 1, k = i & 1, tw = tw0 + k;
+    const bool ok = e < E && tw < nw;
+    const int wb = ok ? wbase[int64_t(e) * nw + tw] : 0;
+    s_wb[k * E4 + e] = wb;
+    s_be[k * E4 + e] = ok ? bits_s[int64_t(e) * nw + tw] : 0u;
+    if (k == 0) before += wb;
   }
   int base;
-  block_excl_scan(before, sh, &base);  // base = sum over all earlier blocks (syncs the LDS)
+  block_excl_scan(before, sh, &base);  // base = slots before the block (syncs the LDS)
+  const int k = tl >> 5;  // this token's word among the block's 2
+  const int b = t & 31;
+  const uint32_t below = (1u << b) - 1u;
+  const uint4* row = reinterpret_cast<const uint4*>(s_be + k * E4);
+  const int wpq = E4 / 128;  // words of 32 experts per quarter
+  // bit i of word w of this token's expert set: expert 32 w + i holds it
+  auto word_of = [&](int w) {
+    uint32_t word = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 q = row[8 * w + i];
+      word |= (((q.x >> b) & 1u) << (4 * i)) | (((q.y >> b) & 1u) << (4 * i + 1)) |
+              (((q.z >> b) & 1u) << (4 * i + 2)) | (((q.w >> b) & 1u) << (4 * i + 3));
+    }
+    return word;
+  };
   int c = 0;
   if (t < T)
-    for (int w = 0; w < W; ++w) c += __popc(s_bt[tid * W + w]);
+    for (int w = sub * wpq; w < (sub + 1) * wpq; ++w) c += __popc(word_of(w));
   int total;
-  const int j0 = base + block_excl_scan(c, sh, &total);
-  if (t < T) token_offsets[t] = j0;
-  if (t == T - 1) token_offsets[T] = j0 + c;
+  int j = base + block_excl_scan(c, sh, &total);
+  if (t < T && sub == 0) token_offsets[t] = j;
+  if (t == T - 1 && sub == 3) token_offsets[T] = j + c;
   if (t >= T) return;
-  const int k = tid >> 5;  // this token's word among the block's 8
-  const uint32_t below = (1u << (t & 31)) - 1u;
-  int j = j0;
-  for (int w = 0; w < W; ++w) {
-    uint32_t m = s_bt[tid * W + w];
+  const int32_t* wbk = s_wb + k * E4;
+  const uint32_t* bek = s_be + k * E4;
+  for (int w = sub * wpq; w < (sub + 1) * wpq; ++w) {
+    uint32_t m = word_of(w);
     while (m) {
-      const int e = w * 32 + __ffs(m) - 1;
+      const int e = 32 * w + __ffs(m) - 1;
       m &= m - 1;
-      token_slots[j++] = s_off[e] + s_wb[e * 8 + k] + __popc(s_be[e * 8 + k] & below);
+      token_slots[j++] = s_off[e] + wbk[e] + __popc(bek[e] & below);
     }
   }
 }
@@ -584,9 +674,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
   char* ws = static_cast<char*>(a.ws);
   uint64_t* keys = reinterpret_cast<uint64_t*>(ws + L.keys);
   uint32_t* bits_e = reinterpret_cast<uint32_t*>(ws + L.bits_e);
-  uint32_t* bits_t = reinterpret_cast<uint32_t*>(ws + L.bits_t);
+  uint32_t* bits_s = reinterpret_cast<uint32_t*>(ws + L.bits_s);
   int32_t* wbase = reinterpret_cast<int32_t*>(ws + L.wbase);
-  int32_t* block_sum = reinterpret_cast<int32_t*>(ws + L.block_sum);
 
   tr.mark(st, 0);
   {
@@ -594,7 +683,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
     const int epl = (E + kTopkLanes - 1) / kTopkLanes;
 #define MOE_TOPK(N)                                                                        \
   hipLaunchKernelGGL(route_topk<N>, grid, dim3(kTopkThreads), 0, st, a.logits, T, E, K,  \
-                     a.topk_ids, keys, bits_e, bits_t)
+                     a.topk_ids, keys, bits_e)
     if (epl <= 1) MOE_TOPK(1);
     else if (epl <= 2) MOE_TOPK(2);
     else if (epl <= 4) MOE_TOPK(4);
@@ -611,17 +700,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st, const TraceHook& tr)
 #define MOE_SELECT(N)                                                                        \
   hipLaunchKernelGGL(route_select<N>, dim3(E + 1), dim3(kSelThreads), 0, st, T, E, a.tc_counts, \
                      a.counts, a.expert_offsets, a.expert_order, a.tile_expert, a.tile_row,    \
-                     a.totals, keys, bits_e, bits_t, wbase, a.slot_token, a.slot_weight,     \
-                     block_sum)
+                     a.totals, keys, bits_e, bits_s, wbase, a.slot_token, a.slot_weight)
   if (T <= 8 * kSelThreads) MOE_SELECT(8);
   else if (T <= 16 * kSelThreads) MOE_SELECT(16);
   else if (T <= 32 * kSelThreads) MOE_SELECT(32);
   else MOE_SELECT(0);
 #undef MOE_SELECT
   tr.mark(st, 3);
-  const size_t tslots_lds = size_t(E) * 4 + size_t(E) * 8 * 4 * 2 + size_t(256) * cdiv(E, 32) * 4;
-  hipLaunchKernelGGL(route_tslots, dim3(cdiv(T, 256)), dim3(256), tslots_lds, st, T, E, bits_t,
-                     bits_e, wbase, a.expert_offsets, block_sum, a.token_offsets, a.token_slots);
+  const size_t tslots_lds = size_t((E + 127) & ~127) * 4 * 5;
+  hipLaunchKernelGGL(route_tslots, dim3(cdiv(T, kCsrTokens)), dim3(256), tslots_lds, st, T, E,
+                     bits_s, wbase, a.expert_offsets, a.token_offsets, a.token_slots);
   tr.mark(st, 4);
   return hipGetLastError();
 }

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(kDlThreads) void k_router_dlogits(
   __shared__ int off[1025];
   __shared__ float g[kDlThreads / 64][64 * EPL];
   for (int i = threadIdx.x; i <= E; i += kDlThreads) off[i] = expert_offsets[i];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index read into a scalar register, so that the token (and the
+  // buffer descriptor over its row) is known to be uniform across the wave
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   const int t = blockIdx.x * (kDlThreads / 64) + w;
   const bool valid = t < Tn;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(

@@ -29,7 +29,7 @@
  *     caller.  The library never allocates or frees memory and keeps no
  *     data between calls.  Its only state is, per device, one stream and
  *     two events that moe_bwd creates on first use and keeps until the
- *     process ends.
+ *     process ends, and the fixed scratch array of moe_route_noalloc.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream).  No call synchronises the host or copies device data to
  *     the host.  Untraced, moe_bwd forks part of its work onto its own
@@ -127,8 +127,8 @@ typedef struct {
  * at least the number of kernels the call launches plus one, the call
  * records trace->events[i] (hipEvent_t, created by the caller) on `stream`
  * before its i-th kernel and trace->events[kernels] after the last one.
- * moe_route launches 4 kernels (top-K, counts, select with the offset scan,
- * token CSR), moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
+ * moe_route launches 4 kernels (top-K, counts, selection with the offset
+ * scan, token CSR), moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
  * dX aggregate, dW1, dW2; the dW segments include the chunk plan and the
  * reduction of split experts), moe_router_fwd 1, moe_router_bwd 4 (dlogits,
  * router dX, dWr partials, dWr reduction).  NULL disables tracing.
