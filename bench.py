@@ -222,7 +222,7 @@ def measure(sh, mode, steps, warmup, dev, T=None, stats=False, traced_only=False
         per += np.array(d)
     per /= steps
     out = {"ms": ms, "per_ms": per, "S": int(rt.totals[0].item()),
-           "tiles": int(rt.totals[1].item())}
+           "tiles": int(rt.totals[1].item()), "E_act": int(np.count_nonzero(rt.counts.cpu().numpy()))}
     if not traced_only:
         out["ms_warm"] = ms_warm
     if stats:
@@ -439,7 +439,8 @@ def main():
     # roofline of the dominant kernel
     dom = int(np.argmax(per))
     dname = names[dom]
-    f_k, b_k = kernel_model(dname, sh, S) or (0, 0)
+    E_act = r["E_act"]
+    f_k, b_k = kernel_model(dname, sh, S, E_act=E_act) or (0, 0)
     t_mfma, t_hbm = f_k / (PEAK_BF16_TFLOPS * 1e12), b_k / (PEAK_HBM_GBS * 1e9)
     dur = per[dom] / 1e3
     if f_k and t_mfma >= t_hbm:
@@ -459,7 +460,7 @@ def main():
 
     kernels = {}
     for k, t in zip(names, per):
-        fk, bk = kernel_model(k, sh, S) or (0, 0)
+        fk, bk = kernel_model(k, sh, S, E_act=E_act) or (0, 0)
         kernels[k] = {"us": round(t * 1e3, 2)}
         if fk:
             kernels[k]["tflops"] = round(fk / (t / 1e3) / 1e12, 1)
@@ -483,7 +484,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{sh.name} MoE layer fwd+bwd, {args.mode.upper()} routing",
                    "T": sh.T, "d": sh.d, "n": sh.n, "E": sh.E, "K": sh.K, "M_tile": sh.M,
-                   "slots": S, "parallelism": "single GPU"},
+                   "slots": S, "active_experts": E_act, "parallelism": "single GPU"},
         "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         # 18 n d per slot actually routed, and per row executed (whole tiles)
         "useful_tflops": 18 * S * sh.n * sh.d / (ms / 1e3) / 1e12,

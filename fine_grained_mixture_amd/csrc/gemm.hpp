@@ -579,6 +579,33 @@ __device__ __forceinline__ int tile_end(const int32_t* __restrict__ tile_row,
   return min(row0 + kTileM, next);
 }
 
+// M-tile mt and column tile nt of linear tile index lin, in expert-major
+// order: an expert with M-tiles [m0, m0 + c) owns the linear range
+// [NT m0, NT (m0 + c)); inside it the M-tiles go in groups of up to G, and
+// a group is walked column tile by column tile (its M-tiles consecutive).
+// The tiles that run at once on one XCD then share the expert's weight
+// block of their column, and a group's row blocks stay in the L2 over its
+// column sweep: each weight block is fetched once per group, each row
+// block once.  The expert of lin is the expert of M-tile lin / NT (inside
+// its range); its M-tiles start at slot rows off_e + i kTileM.
+template <int G>
+__device__ __forceinline__ void grouped_tile(int lin, int NT,
+                                             const int32_t* __restrict__ tile_expert,
+                                             const int32_t* __restrict__ tile_row,
+                                             const int32_t* __restrict__ expert_offsets,
+                                             int& mt, int& nt) {
+  const int g = lin / NT;
+  const int e = tile_expert[g];
+  const int off = expert_offsets[e];
+  const int m0 = g - (tile_row[g] - off) / kTileM;
+  const int c = (expert_offsets[e + 1] - off + kTileM - 1) / kTileM;
+  const int r = lin - NT * m0;
+  const int grp = r / (G * NT), gm = min(G, c - grp * G);
+  const int rr = r - grp * G * NT;
+  nt = rr / gm;
+  mt = m0 + grp * G + rr % gm;
+}
+
 // Spreads `work` logical tiles over the 8 XCDs in contiguous chunks:
 // workgroups are dispatched round-robin over XCDs, so block b runs on XCD
 // b % 8; giving each XCD a contiguous range keeps neighbouring tiles (same

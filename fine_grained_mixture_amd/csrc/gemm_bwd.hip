@@ -193,7 +193,7 @@ template <class Cfg, class T = typename Cfg::T>
 __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
     const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
-    const int32_t* __restrict__ totals, int d,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
     int n, int nslot) {
   static_assert(Cfg::BM == kTileM, "128-row tiles");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
@@ -201,7 +201,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
   const int NT = d / BN, n2 = 2 * n;
   const int lin = xcd_tile(blockIdx.x, totals[1] * NT);
   if (lin < 0) return;
-  const int mt = lin / NT, nt = lin % NT;
+  // W1_e is d x 2n (4 MB at d = 4096, n = 256, as large as the L2): walk
+  // groups of an expert's M-tiles column tile by column tile
+  int mt, nt;
+  grouped_tile<8>(lin, NT, tile_expert, tile_row, expert_offsets, mt, nt);
   const int e = tile_expert[mt], row0 = tile_row[mt];
   const int rend = tile_end(tile_row, totals, mt, row0);
   const int j0 = nt * BN;
@@ -230,8 +233,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
 // is cut into chunks of KC rows, so that no single tile can hold up the end
 // of the kernel; every other expert is one chunk.  A plan lists the chunks
 // ("items") by expert rank (descending slot count, so the largest work starts
-// first); item i carries its expert, its row range and, when the expert is
-// split, the index of its fp32 partial-sum slab.  The PT output tiles of one
+// first; an expert without slots is one item whose tiles only write zeros).
+// Item i carries its expert, its row range and, when the expert is split,
+// the index of its fp32 partial-sum slab.  The PT output tiles of one
 // item stay on one XCD (block b runs on XCD b % 8) so that the item's
 // gathered rows are fetched into one L2.
 struct VarlenItem {
@@ -354,6 +358,21 @@ __device__ __forceinline__ void store_tile_f32(const Accum<Cfg>& acc, float* out
       }
 }
 
+// Zeroes a full weight-gradient tile of an expert that was given no slots
+// (its gradient is exactly zero): whole rows of 16-byte non-temporal
+// stores, without the accumulators and the staging round trip.
+template <class Cfg>
+__device__ __forceinline__ void zero_tile(typename Cfg::T* out, int ld) {
+  constexpr int CPR = Cfg::BN * int(sizeof(typename Cfg::T)) / 16;  // chunks per row
+  static_assert((Cfg::BM * CPR) % Cfg::kThreads == 0, "whole rounds");
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int q = threadIdx.x; q < Cfg::BM * CPR; q += Cfg::kThreads) {
+    char* row = reinterpret_cast<char*>(out + int64_t(q / CPR) * ld);
+    __builtin_nontemporal_store(z, reinterpret_cast<u32x4_t*>(row + (q % CPR) * 16));
+  }
+}
+
 // Writes a full weight-gradient tile (rows i0.., columns j0..) through the
 // epilogue staging buffers.
 template <class Cfg>
@@ -381,6 +400,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw1(
   if (!varlen_item(blockIdx.x, PT, n_items, items, &it, &tile)) return;
   const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
   const int kb = it.kb, ke = it.ke;
+  if (ke == kb) {  // an expert without slots (never split)
+    zero_tile<Cfg>(dW1 + (int64_t(it.e) * d + i0) * n2 + j0, n2);
+    return;
+  }
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
   SlotLoad<Cfg, BM, true> la;
@@ -415,6 +438,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
   if (!varlen_item(blockIdx.x, PT, n_items, items, &it, &tile)) return;
   const int i0 = (tile / TN) * BM, j0 = (tile % TN) * BN;
   const int kb = it.kb, ke = it.ke;
+  if (ke == kb) {  // an expert without slots (never split)
+    zero_tile<Cfg>(dW2 + (int64_t(it.e) * n + i0) * d + j0, d);
+    return;
+  }
   const int nslabs = (ke - kb + Cfg::BK - 1) / Cfg::BK;
 
   SlotLoad<Cfg, BM, false> la;
@@ -471,7 +498,7 @@ void dxt_launch(const LayerArgs& a, const void* dH, const void* W1, void* dXt, h
   hipLaunchKernelGGL((k_dxt<Cfg>), dim3(grid_for(a.tile_cap * (a.d / Cfg::BN))),
                      dim3(Cfg::kThreads), 0, st, static_cast<const T*>(dH),
                      static_cast<const T*>(W1), static_cast<T*>(dXt), a.tile_expert, a.tile_row,
-                     a.totals, a.d, a.n, int(a.slot_cap));
+                     a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
 }
 
 // Tile configurations of the two weight-gradient kernels; f(CfgTag<Cfg>{})

@@ -43,18 +43,22 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
 
-def kernel_model(name, sh, S, esz=2):
+def kernel_model(name, sh, S, esz=2, E_act=None):
     """(FLOPs, bytes) of one launch of kernel `name` for layer shape `sh`
-    with S slots (bf16 when esz = 2), or None for kernels without a model."""
+    with S slots (bf16 when esz = 2), or None for kernels without a model.
+    E_act is the number of experts given at least one slot (default: all):
+    the forward and dH / dX-tilde GEMMs read only those experts' weights,
+    while dW1 / dW2 write the gradient of every expert (zero for the rest)."""
     T, d, n, E = sh.T, sh.d, sh.n, sh.E
+    Ea = E if E_act is None else E_act
     idx = 4 * S  # one int32 per slot
     m = {
-        "up_swiglu": (4 * S * d * n, esz * (S * d + E * d * 2 * n + S * 2 * n + S * n) + idx),
-        "down": (2 * S * n * d, esz * (S * n + E * n * d + S * d)),
+        "up_swiglu": (4 * S * d * n, esz * (S * d + Ea * d * 2 * n + S * 2 * n + S * n) + idx),
+        "down": (2 * S * n * d, esz * (S * n + Ea * n * d + S * d)),
         "aggregate_O": (2 * S * d, esz * (S * d + T * d) + 2 * idx + 4 * T),
-        "dh": (2 * S * d * n, esz * (S * d + E * n * d + S * 2 * n + S * 2 * n + S * n)
+        "dh": (2 * S * d * n, esz * (S * d + Ea * n * d + S * 2 * n + S * 2 * n + S * n)
                + 4 * S + 2 * idx),
-        "dxt": (4 * S * n * d, esz * (S * 2 * n + E * d * 2 * n + S * d)),
+        "dxt": (4 * S * n * d, esz * (S * 2 * n + Ea * d * 2 * n + S * d)),
         "aggregate_dX": (S * d, esz * (S * d + T * d) + idx + 4 * T),
         "dw1": (4 * S * d * n, esz * (S * d + S * 2 * n + E * d * 2 * n) + idx),
         "dw2": (2 * S * n * d, esz * (S * n + S * d + E * n * d) + idx),
@@ -190,7 +194,9 @@ def _traffic_md(args):
            f"FETCH_SIZE = {fs:.3f} x and WRITE_SIZE = {ws:.3f} x its true bytes; the "
            "figures below are divided by those factors.", "",
            f"kernel-sources-sha256: {kernel_sources_sha256()}", "",
-           f"Slots S = {args.slots}.  MB = 1e6 bytes per launch.", "",
+           f"Slots S = {args.slots}; experts with at least one slot: "
+           f"{sh.E if args.active_experts is None else args.active_experts} of {sh.E}.  "
+           "MB = 1e6 bytes per launch.", "",
            "| kernel | launches | read MB | write MB | HBM MB | algorithmic MB | HBM / algorithmic |",
            "|---|---|---|---|---|---|---|"]
     order = ["up_swiglu", "down", "aggregate_O", "dh", "dxt", "aggregate_dX", "dw1", "dw2"]
@@ -199,7 +205,7 @@ def _traffic_md(args):
         if k not in rows:
             continue
         n, rd, wr = rows[k]
-        model = kernel_model(k, sh, args.slots)
+        model = kernel_model(k, sh, args.slots, E_act=args.active_experts)
         alg = f"{model[1] / 1e6:.1f}" if model else "-"
         ratio = f"{(rd + wr) / model[1]:.2f}" if model else "-"
         out.append(f"| {k} | {n} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | "
@@ -218,6 +224,8 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--config", default="7b")
     t.add_argument("--slots", type=int, required=True)
+    t.add_argument("--active-experts", type=int, default=None,
+                   help="experts given at least one slot (default: all)")
     t.add_argument("cmd", nargs="+", help="the commands that produced the CSV files")
     args = ap.parse_args(argv)
     if args.what == "stats":

@@ -40,3 +40,17 @@ def test_intensity_and_saved_bytes_agree_with_the_oracle():
                    - orc.arithmetic_intensity(T, d, n, K, E)) < 1e-9
         assert profiling.activation_bytes(T, d, n, K, T * K)["minimal"] == \
             orc.cached_activation_bytes(T, d, K, n)
+
+
+def test_weight_bytes_follow_the_experts_with_slots():
+    # the GEMMs read the weights of the E_act experts with slots only; the
+    # weight-gradient kernels write the gradients of all E experts (zero
+    # tiles for the rest), whatever E_act is
+    sh = SHAPES["high_sparsity"]
+    S, es = 64384, 2
+    w1, w2 = sh.d * 2 * sh.n * es, sh.n * sh.d * es
+    for k in ("dw1", "dw2"):
+        assert profiling.kernel_model(k, sh, S, E_act=50) == profiling.kernel_model(k, sh, S)
+    for k, w in (("up_swiglu", w1), ("dxt", w1), ("down", w2), ("dh", w2)):
+        full = profiling.kernel_model(k, sh, S)[1]
+        assert full - profiling.kernel_model(k, sh, S, E_act=50)[1] == (sh.E - 50) * w
