@@ -17,6 +17,16 @@
   ``traffic`` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch)
   by what the same counters read for a plain 1 GiB device-to-device copy of
   known traffic (1 GiB read and 1 GiB written per launch).
+
+    python -m fine_grained_mixture_amd.profiling mfma <counter_collection.csv> \
+        --config 7b --slots S <cmd>
+
+  ``mfma`` reads SQ_VALU_MFMA_BUSY_CYCLES (MFMA-pipe cycles summed over every
+  SIMD: a 32x32x16 bf16 MFMA counts 32) and GRBM_GUI_ACTIVE (GPU-busy clock
+  cycles summed over the 8 XCDs) of each dispatch, with the dispatch's own
+  start and end times: MFMA utilisation is the busy cycles over the SIMD
+  cycles the kernel had (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), and the average
+  clock is GRBM_GUI_ACTIVE / 8 over the duration.
 """
 from __future__ import annotations
 
@@ -41,6 +51,8 @@ KERNEL_LABELS = {
 AGGREGATE_LABELS = ("aggregate_O", "aggregate_dX")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
+NUM_XCD, NUM_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
+PEAK_BF16_FLOPS = 2.5e15
 
 
 def kernel_model(name, sh, S, esz=2, E_act=None):
@@ -182,6 +194,65 @@ def _stats_md(path, cmd):
     return "\n".join(out) + "\n"
 
 
+def mfma_table(counters_csv):
+    """Per kernel: (launches, mean duration s, mean MFMA busy cycles, mean
+    GRBM_GUI_ACTIVE) over the dispatches of a counter run that collected
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE."""
+    rows = collections.defaultdict(dict)
+    with open(counters_csv) as fh:
+        for r in csv.DictReader(fh):
+            d = rows[int(r["Dispatch_Id"])]
+            d["name"] = _base_name(r["Kernel_Name"])
+            d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    per = collections.defaultdict(list)
+    n_agg = 0
+    for _, d in sorted(rows.items()):
+        k = d["name"]
+        if k == "k_aggregate":
+            k = AGGREGATE_LABELS[n_agg % 2]
+            n_agg += 1
+        else:
+            k = KERNEL_LABELS.get(k, k)
+        per[k].append(d)
+    out = {}
+    for k, ds in per.items():
+        out[k] = (len(ds), _mean([d["dur"] for d in ds]),
+                  _mean([d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds]),
+                  _mean([d.get("GRBM_GUI_ACTIVE", 0.0) for d in ds]))
+    return out
+
+
+def _mfma_md(args):
+    sys.path.insert(0, ROOT)
+    from fine_grained_mixture_amd.inputs import SHAPES
+
+    sh = SHAPES[args.config]
+    rows = mfma_table(args.csv)
+    out = ["Command (run from /tmp with TMPDIR=/tmp; $R is the repository root):", "",
+           "```", args.cmd, "```", "",
+           f"kernel-sources-sha256: {kernel_sources_sha256()}", "",
+           f"Slots S = {args.slots}.  Durations are the counter run's own (one kernel at a "
+           "time).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
+           "SIMDs); clock = GRBM_GUI_ACTIVE / 8 / duration; TFLOP/s are algorithmic.", "",
+           "| kernel | launches | avg us | MFMA busy | clock GHz | TFLOP/s | of 2.5 PF |",
+           "|---|---|---|---|---|---|---|"]
+    order = ["up_swiglu", "down", "aggregate_O", "dh", "dxt", "aggregate_dX", "dw1", "dw2"]
+    names = order + sorted(k for k in rows if k not in order)
+    for k in names:
+        if k not in rows:
+            continue
+        n, dur, busy, grbm = rows[k]
+        cyc = grbm / NUM_XCD
+        util = busy / (cyc * NUM_SIMD) if cyc > 0 else 0.0
+        clk = cyc / dur / 1e9 if dur > 0 else 0.0
+        model = kernel_model(k, sh, args.slots)
+        tf = f"{model[0] / dur / 1e12:.0f}" if model and model[0] and dur > 0 else "-"
+        frac = f"{model[0] / dur / PEAK_BF16_FLOPS:.3f}" if model and model[0] and dur > 0 else "-"
+        out.append(f"| {k} | {n} | {dur * 1e6:.1f} | {util:.3f} | {clk:.2f} | {tf} | {frac} |")
+    return "\n".join(out) + "\n"
+
+
 def _traffic_md(args):
     sys.path.insert(0, ROOT)
     from fine_grained_mixture_amd.inputs import SHAPES
@@ -227,9 +298,16 @@ def main(argv=None):
     t.add_argument("--active-experts", type=int, default=None,
                    help="experts given at least one slot (default: all)")
     t.add_argument("cmd", nargs="+", help="the commands that produced the CSV files")
+    m = sub.add_parser("mfma", help="MFMA utilisation and clock from SQ / GRBM counters")
+    m.add_argument("csv")
+    m.add_argument("--config", default="7b")
+    m.add_argument("--slots", type=int, required=True)
+    m.add_argument("cmd")
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(_stats_md(args.csv, args.cmd))
+    elif args.what == "mfma":
+        sys.stdout.write(_mfma_md(args))
     else:
         sys.stdout.write(_traffic_md(args))
 

@@ -54,3 +54,19 @@ def test_weight_bytes_follow_the_experts_with_slots():
     for k, w in (("up_swiglu", w1), ("dxt", w1), ("down", w2), ("dh", w2)):
         full = profiling.kernel_model(k, sh, S)[1]
         assert full - profiling.kernel_model(k, sh, S, E_act=50)[1] == (sh.E - 50) * w
+
+
+def test_mfma_table_from_counters(tmp_path):
+    # two dispatches of the up-projection: 2 s of 1e9 busy cycles over
+    # 8 x 1e9 GRBM cycles (1e9 per XCD): 1 GHz, and 1e9 / (1e9 x 1024) busy
+    hdr = ("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,"
+           "End_Timestamp\n")
+    lines = []
+    for i in (1, 2):
+        for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 512e9), ("GRBM_GUI_ACTIVE", 8e9)):
+            lines.append(f'{i},"void moe::k_up_swiglu<cfg>(...)",{c},{v},0,1000000000\n')
+    p = tmp_path / "c.csv"
+    p.write_text(hdr + "".join(lines))
+    (n, dur, busy, grbm), = profiling.mfma_table(str(p)).values()
+    assert n == 2 and dur == 1.0 and busy == 512e9 and grbm == 8e9
+    assert busy / (grbm / profiling.NUM_XCD * profiling.NUM_SIMD) == 0.5
