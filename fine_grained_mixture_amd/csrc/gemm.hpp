@@ -504,11 +504,12 @@ struct RowStage {
   template <class RowPtr>
   __device__ __forceinline__ void fill(RowPtr rowptr) const {
     constexpr int CPR = RB / 16;
+    static_assert((32 * CPR) % 64 == 0, "whole rounds of the wave");
     const int lane = threadIdx.x & 63;
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int idx = lane; idx < 32 * CPR; idx += 64) {
-      const int r = idx / CPR, c = idx % CPR;
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int idx = i * 64 + lane, r = idx / CPR, c = idx % CPR;
       const T* g = rowptr(r);
       if (g) {
         const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(g) + c * 16);
@@ -523,11 +524,12 @@ struct RowStage {
   template <class RowPtr>
   __device__ __forceinline__ void flush(RowPtr rowptr) const {
     constexpr int CPR = RB / 16;
+    static_assert((32 * CPR) % 64 == 0, "whole rounds of the wave");
     const int lane = threadIdx.x & 63;
     asm volatile("" ::: "memory");  // deposits before read-back (LDS keeps wave order)
 #pragma unroll
-    for (int idx = lane; idx < 32 * CPR; idx += 64) {
-      const int r = idx / CPR, c = idx % CPR;
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int idx = i * 64 + lane, r = idx / CPR, c = idx % CPR;
       const char* src = buf + r * LDR + c * 16;
       const uint2 lo = *reinterpret_cast<const uint2*>(src);
       const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
