@@ -108,6 +108,40 @@ def make_layer_inputs(shape: LayerShape | str, dtype=torch.bfloat16, seed=0,
     }
 
 
+ROUTING_LOGIT_KINDS = ("normal", "quantized", "constant", "duplicated", "zipf")
+
+
+def make_routing_logits(T: int, E: int, kind: str, seed: int = 0) -> np.ndarray:
+    """[T, E] float32 router logits for routing-only checks, from numpy PCG64
+    seeded with (seed, 0x7E5):
+      normal      N(0, 1);
+      quantized   N(0, 1) rounded to multiples of 1/4 (many equal logits in a
+                  row, and many equal probabilities across tokens);
+      constant    every logit 0, except that a seeded tenth of the tokens get
+                  N(0, 1) rows;
+      duplicated  N(0, 1) rows, each token a copy of one of T / 8 + 1 rows;
+      zipf        N(0, 1) plus -1.1 ln(rank_e) for a seeded permutation of
+                  ranks 1..E (a few experts hold most tokens)."""
+    rng = np.random.default_rng([seed, 0x7E5])
+    f32 = np.float32
+    z = rng.standard_normal((T, E), dtype=f32)
+    if kind == "normal":
+        out = z
+    elif kind == "quantized":
+        out = np.round(z * f32(4)) / f32(4)
+    elif kind == "constant":
+        out = np.zeros((T, E), dtype=f32)
+        rows = rng.random(T) < 0.1
+        out[rows] = z[rows]
+    elif kind == "duplicated":
+        out = z[rng.integers(0, T // 8 + 1, size=T)]
+    elif kind == "zipf":
+        out = z + (-1.1 * np.log(rng.permutation(E) + 1)).astype(f32)
+    else:
+        raise ValueError(kind)
+    return np.ascontiguousarray(out, dtype=f32)
+
+
 def make_round_rand(E: int, seed: int = 0) -> np.ndarray:
     """The per-expert uniform draws of stochastic token rounding: E values in
     [0, 2**32) from numpy PCG64 seeded with (seed, 0x52D), as uint64.  The
