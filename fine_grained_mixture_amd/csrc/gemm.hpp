@@ -52,15 +52,25 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 template <class T_, int BM_, int BN_, int WGM_, int WGN_, int STAGES_, int KB_ = 128,
-          bool PAIRED_ = false>
+          bool PAIRED_ = false, int NPW_ = 0>
 struct TileCfg {
   using T = T_;
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, KB = KB_;
   static_assert(KB == 64 || KB == 128, "slab bytes");
   static constexpr bool PAIRED = PAIRED_;  // B columns = [gate half | up half]
-  static constexpr int NW = WGM * WGN;  // waves per workgroup
-  static constexpr int kThreads = 64 * NW;
-  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  static constexpr int NW = WGM * WGN;  // compute waves (they hold the accumulators)
+  // Loader waves.  NPW == 0: the compute waves issue their own share of each
+  // slab's DMA.  NPW > 0: waves NW .. NW + NPW - 1 issue all of it and never
+  // multiply, so no compute wave stalls behind the address unit.
+  static constexpr int NPW = NPW_;
+  static constexpr int NLW = NPW > 0 ? NPW : NW;  // waves that issue DMA
+  static constexpr int kThreads = 64 * (NW + NPW);
+  static_assert(NW == 4 || NW == 8, "four or eight compute waves per workgroup");
+  static_assert(NPW == 0 || (NW == 4 && NPW == 4), "four loader waves beside four compute waves");
+  // Wave w's roles.  Waves w and w + 4 share a SIMD, so with loader waves
+  // every SIMD runs one compute wave and one loader wave.
+  __device__ static constexpr bool loads(int w) { return NPW == 0 || w >= NW; }
+  __device__ static constexpr int loader_index(int w) { return NPW == 0 ? w : w - NW; }
   static constexpr int BK = KB / int(sizeof(T));  // k-values per slab
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int MB = WTM / 32, NB = WTN / 32;
@@ -150,20 +160,20 @@ __device__ __forceinline__ int mswz(int k) {
 template <class Cfg, int ROWS>
 struct KLoad {
   static constexpr int KB = Cfg::KB, CPR = KB / 16;  // 16-byte chunks per row
-  static_assert((ROWS * KB) % (Cfg::kThreads * 16) == 0, "rows");
-  static constexpr int NI = ROWS * KB / (Cfg::kThreads * 16);
+  static_assert((ROWS * KB) % (Cfg::NLW * 1024) == 0, "rows");
+  static constexpr int NI = ROWS * KB / (Cfg::NLW * 1024);
   rsrc_t rs;
   uint32_t off[NI];
-  int w;
+  int w;  // index among the waves that issue DMA
 
   template <class RowOff>
   __device__ __forceinline__ void init(const void* base, uint32_t bytes, RowOff rowoff) {
     rs = make_rsrc(base, bytes);
-    w = wave_id();
+    w = Cfg::loader_index(wave_id());
     const int L = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int idx = (i * Cfg::NW + w) * 64 + L;
+      const int idx = (i * Cfg::NLW + w) * 64 + L;
       const int r = idx / CPR, pos = idx % CPR;
       off[i] = uint32_t(rowoff(r)) + uint32_t((pos ^ kswz<KB>(r)) << 4);
     }
@@ -171,7 +181,7 @@ struct KLoad {
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      dma16(rs, off[i] + uint32_t(s * KB), tile + (i * Cfg::NW + w) * 1024);
+      dma16(rs, off[i] + uint32_t(s * KB), tile + (i * Cfg::NLW + w) * 1024);
   }  __device__ __forceinline__ void next(int) const {}
 };
 
@@ -183,23 +193,23 @@ template <class Cfg, int COLS>
 struct MNLoad {
   using T = typename Cfg::T;
   static constexpr int RB = COLS * int(sizeof(T)), CH = RB / 16;
-  static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
-  static_assert(NI >= 1 && (Cfg::BK * RB) % (Cfg::kThreads * 16) == 0, "tile size");
+  static constexpr int NI = Cfg::BK * RB / (Cfg::NLW * 1024);
+  static_assert(NI >= 1 && (Cfg::BK * RB) % (Cfg::NLW * 1024) == 0, "tile size");
   rsrc_t rs;
   uint32_t off[NI];
   uint32_t step;
-  int w;
+  int w;  // index among the waves that issue DMA
 
   template <class ColBytes>
   __device__ __forceinline__ void init(const void* base, uint32_t bytes, uint32_t ld_bytes,
                                        ColBytes col_bytes) {
     rs = make_rsrc(base, bytes);
-    w = wave_id();
+    w = Cfg::loader_index(wave_id());
     const int L = threadIdx.x & 63;
     step = uint32_t(Cfg::BK) * ld_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int idx = (i * Cfg::NW + w) * 64 + L;
+      const int idx = (i * Cfg::NLW + w) * 64 + L;
       const int k = idx / CH, pos = idx % CH;
       off[i] = uint32_t(k) * ld_bytes + uint32_t(col_bytes(pos ^ mswz<CH>(k)));
     }
@@ -207,7 +217,7 @@ struct MNLoad {
   __device__ __forceinline__ void issue(int s, char* tile) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      dma16(rs, off[i] + uint32_t(s) * step, tile + (i * Cfg::NW + w) * 1024);
+      dma16(rs, off[i] + uint32_t(s) * step, tile + (i * Cfg::NLW + w) * 1024);
   }  __device__ __forceinline__ void next(int) const {}
 };
 
@@ -225,6 +235,7 @@ struct SlotLoad {
   static constexpr int NI = Cfg::BK * RB / (Cfg::kThreads * 16);
   static constexpr int RPI = 64 / CH;  // tile rows per DMA instruction
   static_assert(NI >= 1 && RPI >= 1, "tile size");
+  static_assert(Cfg::NPW == 0, "slot-row loads are issued by the compute waves");
   rsrc_t rs;
   const int32_t* idx;
   uint32_t ld_bytes;
@@ -444,6 +455,7 @@ __device__ __forceinline__ void pipeline(Accum<Cfg>& acc, char* lds, int nslabs,
                                          const LB& lb, Tail&& tail) {
   constexpr int S = Cfg::STAGES, NI = LA::NI + LB::NI;
   static_assert(S >= 2 && S <= 4 && NI * (S - 2) < 64, "pipeline depth");
+  static_assert(Cfg::NPW == 0, "tiles with loader waves run persistent_split");
 #pragma unroll
   for (int st = 0; st < S - 1; ++st) {
     if (st < nslabs) {
@@ -472,6 +484,127 @@ __device__ __forceinline__ void pipeline(Accum<Cfg>& acc, char* lds, int nslabs,
                                 s + S - 1, s, la, lb, tail);
   }
   barrier();
+}
+
+// Slab waits of a wave that issued the DMA for slabs up to s + ahead: its own
+// part of slab s has landed once at most `ahead` slabs of NI instructions are
+// still outstanding (the vector-memory counter completes in order).
+template <int S, int NI>
+__device__ __forceinline__ void wait_slab(int ahead) {
+  if constexpr (S >= 4) {
+    if (ahead >= 2) wait_vm<2 * NI>();
+    else if (ahead == 1) wait_vm<NI>();
+    else wait_vm<0>();
+  } else if constexpr (S == 3) {
+    if (ahead >= 1) wait_vm<NI>();
+    else wait_vm<0>();
+  } else {
+    wait_vm<0>();
+  }
+}
+
+// The two loaders of one tile.
+template <class LA, class LB>
+struct LoadPair {
+  LA la;
+  LB lb;
+};
+
+// Tiles one workgroup of a persistent launch keeps descriptors for (in LDS).
+constexpr int kPersistentTiles = 512;
+
+// A persistent launch runs one workgroup per CU.  Workgroup b is on XCD b % 8
+// and takes every (gridDim / 8)-th tile of that XCD's contiguous range,
+// starting at b / 8, so the tiles running at once on an XCD are consecutive
+// (same expert, same weight columns, one L2).  Tile k of the workgroup is
+// first + k * stride.
+struct PersistentShare {
+  int first, stride, ntiles;
+  __device__ static PersistentShare make(int work) {
+    const int per = (work + 7) / 8;
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8, stride = gridDim.x / 8;
+    const int beg = xcd * per + local, end = min(xcd * per + per, work);
+    PersistentShare p;
+    p.first = beg;
+    p.stride = stride;
+    p.ntiles = beg < end ? (end - beg + stride - 1) / stride : 0;
+    return p;
+  }
+  // Largest ntiles of a launch of `grid` workgroups over at most `work` tiles.
+  static int64_t max_tiles(int64_t work, int grid) {
+    return ((work + 7) / 8 + grid / 8 - 1) / (grid / 8);
+  }
+};
+
+// The slab pipeline of a persistent workgroup with loader waves: its ntiles
+// tiles (each of nslabs >= S - 1 slabs) form one stream of slabs.  The loader
+// waves issue and wait for every DMA and run ahead across tile boundaries,
+// so the first S - 1 slabs of the next tile land while the compute waves
+// write the current tile; the compute waves only multiply landed stages and
+// write the outputs.  Both roles pass one barrier per slab and one per tile:
+// the barrier of slab g tells the compute waves that slab g has landed and
+// the loader waves that stage (g - 1) % S is free; the barrier after a
+// tile's last slab frees that slab's stage for the epilogue's staging, until
+// the next slab's barrier.
+//   describe(k)          descriptor of tile k (a trivially copyable struct);
+//                        all are read once into `table` (LDS) at the start
+//   loaders(desc)        the LoadPair of a tile (called in loader waves)
+//   epilogue(desc, acc, stage)  writes a finished tile, staging through the
+//                        STAGE_BYTES at `stage` (called in compute waves)
+template <class Cfg, bool AK, bool BKM, class Tile, class Describe, class Loaders, class Epilogue>
+__device__ __forceinline__ void persistent_split(char* lds, Tile* table, int ntiles, int nslabs,
+                                                 Describe&& describe, Loaders&& loaders,
+                                                 Epilogue&& epilogue) {
+  constexpr int S = Cfg::STAGES;
+  static_assert(Cfg::NPW > 0, "tiles with loader waves");
+  for (int k = threadIdx.x; k < ntiles; k += Cfg::kThreads) table[k] = describe(k);
+  __syncthreads();
+  const int G = ntiles * nslabs;  // slabs in the stream
+  if (Cfg::loads(wave_id())) {
+    auto cur = loaders(table[0]);
+    auto nxt = loaders(table[ntiles > 1 ? 1 : 0]);
+    using LP = decltype(cur);
+    constexpr int NI = decltype(cur.la)::NI + decltype(cur.lb)::NI;
+    static_assert(S >= 2 && S <= 4 && NI * (S - 2) < 64, "pipeline depth");
+    auto issue = [&](const LP& p, int j, int g) {  // slab j of p's tile is slab g of the stream
+      char* sp = lds + (g % S) * Cfg::STAGE_BYTES;
+      p.la.issue(j, sp);
+      p.lb.issue(j, sp + Cfg::A_BYTES);
+    };
+    for (int g = 0; g < S - 1 && g < G; ++g) {
+      if (g < nslabs) issue(cur, g, g);
+      else issue(nxt, g - nslabs, g);
+    }
+    for (int k = 0; k < ntiles; ++k) {
+      for (int j = 0; j < nslabs; ++j) {
+        const int g = k * nslabs + j;
+        wait_slab<S, NI>(min(S - 2, G - 1 - g));
+        barrier();
+        if (g + S - 1 < G) {
+          if (j + S - 1 < nslabs) issue(cur, j + S - 1, g + S - 1);
+          else issue(nxt, j + S - 1 - nslabs, g + S - 1);
+        }
+      }
+      barrier();  // the compute waves write tile k
+      if (k + 1 < ntiles) {
+        cur = nxt;
+        if (k + 2 < ntiles) nxt = loaders(table[k + 2]);
+      }
+    }
+    return;
+  }
+  Accum<Cfg> acc;
+  for (int k = 0; k < ntiles; ++k) {
+    const Tile desc = table[k];
+    acc.init();
+    for (int j = 0; j < nslabs; ++j) {
+      barrier();
+      const char* cur = lds + ((k * nslabs + j) % S) * Cfg::STAGE_BYTES;
+      acc.template slab<AK, BKM>(cur, cur + Cfg::A_BYTES);
+    }
+    barrier();  // every compute wave is done with the last slab's stage
+    epilogue(desc, acc, lds + ((k * nslabs + nslabs - 1) % S) * Cfg::STAGE_BYTES);
+  }
 }
 
 struct NoTail {

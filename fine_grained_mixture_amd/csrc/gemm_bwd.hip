@@ -229,6 +229,57 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt(
   });
 }
 
+// dX-tilde as a persistent launch with loader waves (one workgroup per CU,
+// Cfg::NPW > 0): the same tiles, in the same grouped order, walked by each
+// workgroup in turn, so the next tile's first slabs are in flight while this
+// tile's rows are written.
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dxt_p(
+    const T* __restrict__ dH, const T* __restrict__ W1, T* __restrict__ dXt,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ totals, int d,
+    int n, int nslot) {
+  static_assert(Cfg::BM == kTileM && Cfg::NPW > 0, "128-row tiles with loader waves");
+  struct Tile {
+    int e, row0, rend, j0;
+  };
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  __shared__ Tile table[kPersistentTiles];
+  constexpr int BN = Cfg::BN;
+  const int NT = d / BN, n2 = 2 * n;
+  const PersistentShare ps = PersistentShare::make(totals[1] * NT);
+  if (ps.ntiles == 0 || ps.ntiles > kPersistentTiles) return;  // the host keeps it in range
+  auto describe = [&](int k) {
+    int mt, nt;
+    grouped_tile<8>(ps.first + k * ps.stride, NT, tile_expert, tile_row, expert_offsets, mt, nt);
+    Tile t;
+    t.e = tile_expert[mt];
+    t.row0 = tile_row[mt];
+    t.rend = tile_end(tile_row, totals, mt, t.row0);
+    t.j0 = nt * BN;
+    return t;
+  };
+  const uint32_t hrow = uint32_t(n2) * sizeof(T);
+  auto loaders = [&](const Tile& t) {
+    LoadPair<KLoad<Cfg, kTileM>, KLoad<Cfg, BN>> p;
+    p.la.init(dH, uint32_t(nslot) * hrow, [&](int r) {
+      const int slot = t.row0 + r;
+      return uint32_t(slot < t.rend ? slot : t.row0) * hrow;
+    });
+    p.lb.init(W1 + int64_t(t.e) * d * n2, uint32_t(d) * hrow,
+              [&](int c) { return uint32_t(t.j0 + c) * hrow; });
+    return p;
+  };
+  auto epilogue = [&](const Tile& t, const Accum<Cfg>& acc, char* stage) {
+    static_assert(RowStage<T, Cfg::WTN>::BYTES * Cfg::NW <= Cfg::STAGE_BYTES, "staging fits");
+    store_acc_staged(acc, stage, [&](int r) -> T* {
+      return t.row0 + r < t.rend ? dXt + int64_t(t.row0 + r) * d + t.j0 : nullptr;
+    });
+  };
+  persistent_split<Cfg, true, true>(lds, table, ps.ntiles, n2 / Cfg::BK, describe, loaders,
+                                    epilogue);
+}
+
 // Varlen-K scheduling.  The contraction of an expert with more than KC rows
 // is cut into chunks of KC rows, so that no single tile can hold up the end
 // of the kernel; every other expert is one chunk.  A plan lists the chunks
@@ -618,7 +669,14 @@ hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const v
 
 hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
                       hipStream_t st) {
-  if (a.f32) dxt_launch<TileCfg<float, kTileM, 128, 2, 2, 3>>(a, dH, W1, dXt, st);
+  using P = RowsSplit;
+  if (!a.f32 && a.d % P::BN == 0 && 2 * a.n / P::BK >= P::STAGES - 1 &&
+      PersistentShare::max_tiles(a.tile_cap * (a.d / P::BN), kNumCUs) <= kPersistentTiles) {
+    hipLaunchKernelGGL((k_dxt_p<P>), dim3(kNumCUs), dim3(P::kThreads), 0, st,
+                       static_cast<const bf16_t*>(dH), static_cast<const bf16_t*>(W1),
+                       static_cast<bf16_t*>(dXt), a.tile_expert, a.tile_row, a.expert_offsets,
+                       a.totals, a.d, a.n, int(a.slot_cap));
+  } else if (a.f32) dxt_launch<TileCfg<float, kTileM, 128, 2, 2, 3>>(a, dH, W1, dXt, st);
   else if (a.d % 512 == 0) dxt_launch<RowsWide>(a, dH, W1, dXt, st);
   else if (a.d % 256 == 0) dxt_launch<RowsMid>(a, dH, W1, dXt, st);
   else dxt_launch<RowsNarrow>(a, dH, W1, dXt, st);

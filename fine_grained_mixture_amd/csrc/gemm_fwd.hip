@@ -132,6 +132,56 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_down(
   });
 }
 
+// The down-projection as a persistent launch with loader waves (one
+// workgroup per CU, Cfg::NPW > 0): the same tiles, each workgroup walking its
+// share in turn, so the next tile's first slabs land while this tile's rows
+// are written.
+template <class Cfg, class T = typename Cfg::T>
+__global__ __launch_bounds__(Cfg::kThreads) void k_down_p(
+    const T* __restrict__ Aact, const T* __restrict__ W2, T* __restrict__ Y,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ totals, int d, int n, int nslot) {
+  static_assert(Cfg::BM == kTileM && Cfg::NPW > 0, "128-row tiles with loader waves");
+  struct Tile {
+    int e, row0, rend, j0;
+  };
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  __shared__ Tile table[kPersistentTiles];
+  constexpr int BN = Cfg::BN, EPC = 16 / int(sizeof(T));
+  const int NT = d / BN;
+  const PersistentShare ps = PersistentShare::make(totals[1] * NT);
+  if (ps.ntiles == 0 || ps.ntiles > kPersistentTiles) return;  // the host keeps it in range
+  auto describe = [&](int k) {
+    const int lin = ps.first + k * ps.stride;
+    const int mt = lin / NT, nt = lin % NT;
+    Tile t;
+    t.e = tile_expert[mt];
+    t.row0 = tile_row[mt];
+    t.rend = tile_end(tile_row, totals, mt, t.row0);
+    t.j0 = nt * BN;
+    return t;
+  };
+  const uint32_t arow = uint32_t(n) * sizeof(T);
+  auto loaders = [&](const Tile& t) {
+    LoadPair<KLoad<Cfg, kTileM>, MNLoad<Cfg, BN>> p;
+    p.la.init(Aact, uint32_t(nslot) * arow, [&](int r) {
+      const int slot = t.row0 + r;
+      return uint32_t(slot < t.rend ? slot : t.row0) * arow;
+    });
+    p.lb.init(W2 + int64_t(t.e) * n * d, uint32_t(n) * d * sizeof(T), uint32_t(d) * sizeof(T),
+              [&](int c) { return int((t.j0 + c * EPC) * sizeof(T)); });
+    return p;
+  };
+  auto epilogue = [&](const Tile& t, const Accum<Cfg>& acc, char* stage) {
+    static_assert(RowStage<T, Cfg::WTN>::BYTES * Cfg::NW <= Cfg::STAGE_BYTES, "staging fits");
+    store_acc_staged(acc, stage, [&](int r) -> T* {
+      return t.row0 + r < t.rend ? Y + int64_t(t.row0 + r) * d + t.j0 : nullptr;
+    });
+  };
+  persistent_split<Cfg, true, false>(lds, table, ps.ntiles, n / Cfg::BK, describe, loaders,
+                                     epilogue);
+}
+
 inline unsigned grid_for(int64_t work) { return unsigned(((work + 7) / 8) * 8); }
 
 template <class Cfg>
@@ -168,7 +218,14 @@ hipError_t launch_up_swiglu(const LayerArgs& a, const void* X, const void* W1, v
 
 hipError_t launch_down(const LayerArgs& a, const void* Aact, const void* W2, void* Y,
                        hipStream_t st) {
-  if (a.f32) down_launch<TileCfg<float, kTileM, 128, 2, 2, 3>>(a, Aact, W2, Y, st);
+  using P = RowsSplit;
+  if (!a.f32 && a.d % P::BN == 0 && a.n / P::BK >= P::STAGES - 1 &&
+      PersistentShare::max_tiles(a.tile_cap * (a.d / P::BN), kNumCUs) <= kPersistentTiles) {
+    hipLaunchKernelGGL((k_down_p<P>), dim3(kNumCUs), dim3(P::kThreads), 0, st,
+                       static_cast<const bf16_t*>(Aact), static_cast<const bf16_t*>(W2),
+                       static_cast<bf16_t*>(Y), a.tile_expert, a.tile_row, a.totals, a.d, a.n,
+                       int(a.slot_cap));
+  } else if (a.f32) down_launch<TileCfg<float, kTileM, 128, 2, 2, 3>>(a, Aact, W2, Y, st);
   else if (a.d % 512 == 0) down_launch<RowsWide>(a, Aact, W2, Y, st);
   else if (a.d % 256 == 0) down_launch<RowsMid>(a, Aact, W2, Y, st);
   else down_launch<RowsNarrow>(a, Aact, W2, Y, st);

@@ -1,11 +1,13 @@
 // Tile shapes of the bf16 grouped GEMMs (fp32 problems use fixed small
 // tiles in the launchers).  TileCfg<T, BM, BN, waves along M, waves along N,
-// pipeline stages, slab bytes KB, paired gate|up columns>.
+// pipeline stages, slab bytes KB, paired gate|up columns, loader waves>.
 //
 //   UpWide/Mid/Narrow   up-projection: 128 slot rows x (gate half | up half),
 //                       half = 256 / 128 / 64 gate columns
 //   RowsWide/Mid/Narrow down-projection and dX-tilde: 128 slot rows x 512 /
 //                       256 / 128 output columns
+//   RowsSplit           the same, 128 x 256, four compute and four loader
+//                       waves, in persistent launches (one workgroup per CU)
 //   DhWide              dH for n = 256: 128 slot rows x all 256 columns
 //   GradSquare/Tall/Small  dW1 / dW2 (varlen-K): 256x256 / 128x256 / 128x128
 #pragma once
@@ -18,6 +20,8 @@ namespace moe {
 // tiles, three for dH (whose H reloads in the epilogue favour a deeper ring)
 using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
 using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
+// three 48 KB stages; loader waves 4-7 beside compute waves 0-3
+using RowsSplit = TileCfg<bf16_t, 128, 256, 2, 2, 3, 128, false, 4>;
 using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
 using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 
