@@ -669,8 +669,11 @@ hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const v
 
 hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
                       hipStream_t st) {
+  // The persistent tile is 256 columns wide, so every dH row block is read
+  // d / 256 times; past 2048 columns that re-reading costs more than the
+  // overlap gains (measured at d = 4096), and the 512-wide tiles run instead.
   using P = RowsSplit;
-  if (!a.f32 && a.d % P::BN == 0 && 2 * a.n / P::BK >= P::STAGES - 1 &&
+  if (!a.f32 && a.d % P::BN == 0 && a.d <= 2048 && 2 * a.n / P::BK >= P::STAGES - 1 &&
       PersistentShare::max_tiles(a.tile_cap * (a.d / P::BN), kNumCUs) <= kPersistentTiles) {
     hipLaunchKernelGGL((k_dxt_p<P>), dim3(kNumCUs), dim3(P::kThreads), 0, st,
                        static_cast<const bf16_t*>(dH), static_cast<const bf16_t*>(W1),

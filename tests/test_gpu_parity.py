@@ -57,6 +57,12 @@ EXTRA = {
     # the largest K and the largest M_tile the library takes
     "k32": LayerShape("k32", 512, 128, 64, 64, 32, 16, "fan_in", "iid"),
     "m1024": LayerShape("m1024", 2048, 128, 64, 8, 4, 1024, "fan_in", "iid"),
+    # launch boundaries of the persistent kernels: dX-tilde persistent with its
+    # fewest slabs (2n / 64 = 2) at the widest d it takes (2048) while the
+    # down-projection, with one slab, runs the per-tile kernel ...
+    "d2048_n64": LayerShape("d2048_n64", 700, 2048, 64, 16, 2, 64, "fan_in", "normal_bias"),
+    # ... and d past 2048: dX-tilde per tile, the down-projection persistent
+    "d2304": LayerShape("d2304", 640, 2304, 128, 8, 2, 32, "fan_in", "iid"),
 }
 KIND = {torch.bfloat16: "bf16", torch.float32: "f32"}
 ORC_MODE = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
@@ -181,6 +187,7 @@ def nonfinite_logits(logits, seed=7):
 
 
 SMALL_CASES = SMALL_CASES + [
+    ("d2048_n64", torch.bfloat16, "tr"), ("d2304", torch.bfloat16, "tc"),
     ("long_t", torch.bfloat16, "tr"), ("long_t", torch.bfloat16, "tc"),
     ("long_t", torch.bfloat16, "tr_stochastic"),
     ("k32", torch.bfloat16, "tr"), ("k32", torch.float32, "tc"),
