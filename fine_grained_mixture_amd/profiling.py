@@ -27,6 +27,18 @@
   start and end times: MFMA utilisation is the busy cycles over the SIMD
   cycles the kernel had (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), and the average
   clock is GRBM_GUI_ACTIVE / 8 over the duration.
+
+    python -m fine_grained_mixture_amd.profiling pipeline --csv C1.csv --csv C2.csv ... <cmd> ...
+
+  ``pipeline`` summarises the vector-memory path of each kernel from the
+  counter runs given (any split of the counters over runs): the mean latency
+  of an L1 -> L2 read request (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ, in
+  cycles), the read requests per CU per cycle, their product (requests in
+  flight per CU), the L2 hit rate, the mean latency of an L2 -> memory read
+  (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ), and the busy fractions of the
+  address (TA) and data (TD) units, of TD waiting on the L1, and of the L1
+  waiting on the L2 (TCP_PENDING_STALL_CYCLES), each per CU over the kernel's
+  cycles (GRBM_GUI_ACTIVE / 8).
 """
 from __future__ import annotations
 
@@ -286,6 +298,73 @@ def _traffic_md(args):
     return "\n".join(out) + "\n"
 
 
+PIPELINE_COUNTERS = (
+    "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", "TCP_PENDING_STALL_CYCLES_sum",
+    "TA_BUSY_avr", "TD_TD_BUSY_sum", "TD_TC_STALL_sum", "TCC_HIT_sum", "TCC_MISS_sum",
+    "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum", "GRBM_GUI_ACTIVE")
+
+
+def pipeline_table(csvs):
+    """Per kernel label: (launches, mean duration s, {counter: mean value per
+    dispatch}) over one or more counter runs of the same program."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(list)
+    for path in csvs:
+        rows = collections.defaultdict(dict)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                d = rows[int(r["Dispatch_Id"])]
+                d["name"] = _base_name(r["Kernel_Name"])
+                d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+        n_agg = 0
+        for _, d in sorted(rows.items()):
+            k = d["name"]
+            if k == "k_aggregate":
+                k = AGGREGATE_LABELS[n_agg % 2]
+                n_agg += 1
+            else:
+                k = KERNEL_LABELS.get(k, k)
+            durs[k].append(d["dur"])
+            for c, v in d.items():
+                if c not in ("name", "dur"):
+                    per[k][c].append(v)
+    return {k: (len(durs[k]) // max(1, len(csvs)), _mean(durs[k]),
+                {c: _mean(v) for c, v in per[k].items()}) for k in per}
+
+
+def _pipeline_md(args):
+    rows = pipeline_table(args.csv)
+    out = ["Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root):", "",
+           "```", *args.cmd, "```", "",
+           f"kernel-sources-sha256: {kernel_sources_sha256()}", "",
+           "Per launch, averaged over launches; cycles are GPU clock cycles; \"per CU\" "
+           "fractions are of the kernel's cycles (GRBM_GUI_ACTIVE / 8) on each of the 256 CUs.",
+           "",
+           "| kernel | avg us | L2 read latency (cyc) | L2 reads per CU per cyc | "
+           "in flight per CU | L2 hit | memory read latency (cyc) | TA busy | TD busy | "
+           "TD waits on L1 | L1 waits on L2 |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    order = ["up_swiglu", "down", "aggregate_O", "dh", "dxt", "aggregate_dX", "dw1", "dw2"]
+    for k in order:
+        if k not in rows:
+            continue
+        _, dur, v = rows[k]
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / NUM_XCD
+        if not cyc:
+            continue
+        cu = cyc * (NUM_SIMD // 4)
+        lat = v["TCP_TCC_READ_REQ_LATENCY_sum"] / v["TCP_TCC_READ_REQ_sum"]
+        rate = v["TCP_TCC_READ_REQ_sum"] / cu
+        hit = v["TCC_HIT_sum"] / (v["TCC_HIT_sum"] + v["TCC_MISS_sum"])
+        mlat = v["TCC_EA0_RDREQ_LEVEL_sum"] / v["TCC_EA0_RDREQ_sum"]
+        out.append(f"| {k} | {dur * 1e6:.1f} | {lat:.0f} | {rate:.3f} | {lat * rate:.0f} | "
+                   f"{hit:.2f} | {mlat:.0f} | {v['TA_BUSY_avr'] / cyc:.2f} | "
+                   f"{v['TD_TD_BUSY_sum'] / cu:.2f} | {v['TD_TC_STALL_sum'] / cu:.2f} | "
+                   f"{v['TCP_PENDING_STALL_CYCLES_sum'] / cu:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -305,11 +384,16 @@ def main(argv=None):
     m.add_argument("--config", default="7b")
     m.add_argument("--slots", type=int, required=True)
     m.add_argument("cmd")
+    q = sub.add_parser("pipeline", help="vector-memory path summary from counter runs")
+    q.add_argument("--csv", action="append", required=True, help="one counter CSV (repeat)")
+    q.add_argument("cmd", nargs="+", help="the commands that produced the CSV files")
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(_stats_md(args.csv, args.cmd))
     elif args.what == "mfma":
         sys.stdout.write(_mfma_md(args))
+    elif args.what == "pipeline":
+        sys.stdout.write(_pipeline_md(args))
     else:
         sys.stdout.write(_traffic_md(args))
 

@@ -70,3 +70,32 @@ def test_mfma_table_from_counters(tmp_path):
     (n, dur, busy, grbm), = profiling.mfma_table(str(p)).values()
     assert n == 2 and dur == 1.0 and busy == 512e9 and grbm == 8e9
     assert busy / (grbm / profiling.NUM_XCD * profiling.NUM_SIMD) == 0.5
+
+
+def test_pipeline_summary_from_counters(tmp_path):
+    # one dispatch of the persistent dX-tilde over 1e6 cycles per XCD, its
+    # counters split over two runs: 2.56e7 L2 reads of 500 cycles each is
+    # 0.1 reads per CU per cycle and 50 in flight; 3 hits per miss
+    hdr = ("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,"
+           "End_Timestamp\n")
+    cu_cyc = 1e6 * 256
+    runs = [(("TCP_TCC_READ_REQ_LATENCY_sum", 500 * 2.56e7), ("TCP_TCC_READ_REQ_sum", 2.56e7),
+             ("TCP_PENDING_STALL_CYCLES_sum", 0.25 * cu_cyc), ("TA_BUSY_avr", 0.5e6),
+             ("GRBM_GUI_ACTIVE", 8e6)),
+            (("TD_TD_BUSY_sum", 0.75 * cu_cyc), ("TD_TC_STALL_sum", 0.4 * cu_cyc),
+             ("TCC_HIT_sum", 3e6), ("TCC_MISS_sum", 1e6), ("TCC_EA0_RDREQ_LEVEL_sum", 9e8),
+             ("TCC_EA0_RDREQ_sum", 1e6), ("GRBM_GUI_ACTIVE", 8e6))]
+    paths = []
+    for i, counters in enumerate(runs):
+        p = tmp_path / f"p{i}.csv"
+        p.write_text(hdr + "".join(
+            f'1,"void moe::k_dxt_p<cfg>(...)",{c},{v},0,500000\n' for c, v in counters))
+        paths.append(str(p))
+    (label, (n, dur, v)), = profiling.pipeline_table(paths).items()
+    assert label == "dxt" and n == 1 and dur == 5e-4
+
+    class Args:
+        csv = paths
+        cmd = ["run 1", "run 2"]
+    row = [l for l in profiling._pipeline_md(Args).splitlines() if l.startswith("| dxt |")]
+    assert row == ["| dxt | 500.0 | 500 | 0.100 | 50 | 0.75 | 900 | 0.50 | 0.75 | 0.40 | 0.25 |"]
