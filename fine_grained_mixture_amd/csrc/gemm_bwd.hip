@@ -280,6 +280,135 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt_p(
                                     epilogue);
 }
 
+// dX-tilde with the A operand in registers: a persistent launch (one
+// workgroup per CU) over whole M tiles.  Each of the four compute waves reads
+// its 32 dH rows (all 2n = 64 NSK k-values) once per M tile straight into
+// MFMA operand registers, then sweeps the output columns in chunks of BN:
+// the loader waves stream only W1_e (BN rows x 128 bytes per slab, K-major)
+// through a ring of S stages, so a slab carries B alone and every B byte is
+// used by all 128 rows of the tile.  A stage holds SUB consecutive k slabs,
+// so the workgroup meets at a barrier once per SUB slabs.  A compute wave
+// writes each finished 32 x BN chunk through its own staging buffer beside
+// the ring.
+template <class Cfg, int NSK, int SUB>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dxt_r(
+    const bf16_t* __restrict__ dH, const bf16_t* __restrict__ W1, bf16_t* __restrict__ dXt,
+    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row,
+    const int32_t* __restrict__ totals, int d, int n, int nslot) {
+  using T = bf16_t;
+  static_assert(Cfg::BM == kTileM && Cfg::NPW > 0 && Cfg::WGN == 1 && Cfg::MB == 1,
+                "whole 128-row tiles, one 32-row block per compute wave, loader waves");
+  static_assert(NSK % SUB == 0, "whole stages per column chunk");
+  constexpr int S = Cfg::STAGES, BN = Cfg::BN, SLAB = Cfg::B_BYTES, STAGE = SUB * SLAB;
+  constexpr int NST = NSK / SUB;  // stages per column chunk
+  using St = RowStage<T, Cfg::WTN>;
+  struct Tile {
+    int e, row0, rend;
+  };
+  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + Cfg::NW * St::BYTES];
+  __shared__ Tile table[kPersistentTiles];
+  const int n2 = 2 * n, NC = d / BN;
+  const PersistentShare ps = PersistentShare::make(totals[1]);
+  if (ps.ntiles == 0 || ps.ntiles > kPersistentTiles) return;  // the host keeps it in range
+  for (int k = threadIdx.x; k < ps.ntiles; k += Cfg::kThreads) {
+    const int mt = ps.first + k * ps.stride;
+    Tile t;
+    t.e = tile_expert[mt];
+    t.row0 = tile_row[mt];
+    t.rend = tile_end(tile_row, totals, mt, t.row0);
+    table[k] = t;
+  }
+  __syncthreads();
+  const int per_tile = NC * NST;  // stages per M tile
+  const int G = ps.ntiles * per_tile;
+  const uint32_t hrow = uint32_t(n2) * sizeof(T);
+  if (Cfg::loads(wave_id())) {
+    // Stage fill g holds k slabs SUB (g % NST) .. of column chunk
+    // (g % per_tile) / NST of M tile g / per_tile.  The loader waves read no LDS (an LDS read after a DMA
+    // into LDS would wait for every DMA in flight); each M tile's expert
+    // comes from a scalar load issued one tile ahead.
+    using LB = KLoad<Cfg, BN>;
+    constexpr int NI = LB::NI, CPR = Cfg::KB / 16;
+    const int lw = Cfg::loader_index(wave_id()), lane = threadIdx.x & 63;
+    uint32_t boff[NI];  // W1 row r of the chunk and its swizzled 16-byte chunk
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = (i * Cfg::NLW + lw) * 64 + lane, r = idx / CPR, pos = idx % CPR;
+      boff[i] = uint32_t(r) * hrow + uint32_t((pos ^ kswz<Cfg::KB>(r)) << 4);
+    }
+    auto expert = [&](int k) { return tile_expert[ps.first + min(k, ps.ntiles - 1) * ps.stride]; };
+    int kc = 0, ec = expert(0), en = expert(1);
+    auto issue = [&](int g) {
+      const int k = g / per_tile, c = (g % per_tile) / NST, s = (g % NST) * SUB;
+      if (k != kc) {  // the next M tile: its expert was read one tile ago
+        kc = k;
+        ec = en;
+        en = expert(k + 1);
+      }
+      const rsrc_t rs = make_rsrc(W1 + int64_t(ec) * d * n2, uint32_t(d) * hrow);
+      char* stage = lds + (g % S) * STAGE;
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const uint32_t add = uint32_t(c * BN) * hrow + uint32_t((s + u) * Cfg::KB);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          dma16(rs, boff[i] + add, stage + u * SLAB + (i * Cfg::NLW + lw) * 1024);
+      }
+    };
+    for (int g = 0; g < S - 1 && g < G; ++g) issue(g);
+    for (int g = 0; g < G; ++g) {
+      wait_slab<S, NI * SUB>(min(S - 2, G - 1 - g));
+      barrier();
+      if (g + S - 1 < G) issue(g + S - 1);
+    }
+    return;
+  }
+  Accum<Cfg> acc;
+  const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
+  const int w = wave_id();
+  char* stg = lds + S * STAGE;
+  for (int k = 0; k < ps.ntiles; ++k) {
+    const Tile t = table[k];
+    // this lane's dH row (rows past the expert read the tile's first row),
+    // k-values 16 c + 8 h .. + 7 of every 16-wide chunk c: the A operand
+    const int row = t.row0 + w * 32 + r32;
+    const T* src = dH + int64_t(row < t.rend ? row : t.row0) * n2 + 8 * h;
+    Oct<T> a[4 * NSK];
+#pragma unroll
+    for (int c = 0; c < 4 * NSK; ++c) oct_load(a[c], src + 16 * c);
+    for (int c = 0; c < NC; ++c) {
+      acc.init();
+#pragma unroll
+      for (int s = 0; s < NST; ++s) {
+        barrier();
+        const char* B0 = lds + (((k * NC + c) * NST + s) % S) * STAGE;
+        // the fragments of k chunk q + 1 are read while chunk q multiplies
+        constexpr int NQ = SUB * Cfg::KCH;
+        Oct<T> fb[2][Cfg::NB];
+#pragma unroll
+        for (int nb = 0; nb < Cfg::NB; ++nb) frag_k<T, Cfg::KB>(fb[0][nb], B0, nb * 32 + r32, 0, h);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if (q + 1 < NQ) {
+            const char* B = B0 + ((q + 1) / Cfg::KCH) * SLAB;
+#pragma unroll
+            for (int nb = 0; nb < Cfg::NB; ++nb)
+              frag_k<T, Cfg::KB>(fb[(q + 1) & 1][nb], B, nb * 32 + r32, (q + 1) % Cfg::KCH, h);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int nb = 0; nb < Cfg::NB; ++nb)
+            mma16(acc.acc[0][nb], fb[q & 1][nb], a[s * NQ + q]);
+        }
+      }
+      const int j0 = c * BN;
+      store_acc_staged(acc, stg, [&](int r) -> T* {
+        return t.row0 + r < t.rend ? dXt + int64_t(t.row0 + r) * d + j0 : nullptr;
+      });
+    }
+  }
+}
+
 // Varlen-K scheduling.  The contraction of an expert with more than KC rows
 // is cut into chunks of KC rows, so that no single tile can hold up the end
 // of the kernel; every other expert is one chunk.  A plan lists the chunks
@@ -669,6 +798,23 @@ hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const v
 
 hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
                       hipStream_t st) {
+  // dH rows in registers (2n <= 512, so they fit in 128 registers per lane),
+  // else the persistent 256-wide tiles up to d = 2048, else the per-tile
+  // 512-wide ones.
+  using R = RowsReg;
+  const bool reg_tiles = PersistentShare::max_tiles(a.tile_cap, kNumCUs) <= kPersistentTiles;
+  if (!a.f32 && a.d % R::BN == 0 && reg_tiles && (a.n == 64 || a.n == 128 || a.n == 256)) {
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(kNumCUs), dim3(R::kThreads), 0, st,
+                         static_cast<const bf16_t*>(dH), static_cast<const bf16_t*>(W1),
+                         static_cast<bf16_t*>(dXt), a.tile_expert, a.tile_row, a.totals, a.d,
+                         a.n, int(a.slot_cap));
+    };
+    if (a.n == 256) go(k_dxt_r<R, 8, 2>);
+    else if (a.n == 128) go(k_dxt_r<R, 4, 2>);
+    else go(k_dxt_r<R, 2, 2>);
+    return hipGetLastError();
+  }
   // The persistent tile is 256 columns wide, so every dH row block is read
   // d / 256 times; past 2048 columns that re-reading costs more than the
   // overlap gains (measured at d = 4096), and the 512-wide tiles run instead.

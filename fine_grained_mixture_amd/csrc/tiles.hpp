@@ -22,6 +22,9 @@ using UpWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128, true>;
 using RowsWide = TileCfg<bf16_t, 128, 512, 2, 4, 2, 128>;
 // three 48 KB stages; loader waves 4-7 beside compute waves 0-3
 using RowsSplit = TileCfg<bf16_t, 128, 256, 2, 2, 3, 128, false, 4>;
+// dX-tilde with the dH rows in registers: 32 x 128 per compute wave, W1
+// slabs of 16 KB, two per stage, in a three-stage ring
+using RowsReg = TileCfg<bf16_t, 128, 128, 4, 1, 3, 128, false, 4>;
 using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
 using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 

@@ -59,7 +59,7 @@ KERNEL_LABELS = {
     "k_up_swiglu": "up_swiglu", "k_down": "down", "k_dh": "dh", "k_dxt": "dxt",
     "k_dw1": "dw1", "k_dw2": "dw2",
     # persistent launches of the same steps
-    "k_down_p": "down", "k_dxt_p": "dxt",
+    "k_down_p": "down", "k_dxt_p": "dxt", "k_dxt_r": "dxt",
 }
 # the aggregation kernel runs twice per step: forward (O), then backward (dX)
 AGGREGATE_LABELS = ("aggregate_O", "aggregate_dX")
