@@ -476,6 +476,107 @@ __global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(
   plan_one(offsets, order, E, kc2, header2, items2, splits2, sh);
 }
 
+// Schedules of the persistent weight-gradient kernels (one workgroup per
+// plan; a plan with cap == 0 has none).  Every (item, tile) pair of a plan
+// goes to one of the 256 workgroups, balancing their work by the longest-
+// first greedy rule: the items (listed by the plan in descending size) go
+// one after another to the XCD with the least work so far, so all tiles of
+// an item and its gathered rows stay in one L2; then, per XCD, the PT
+// tiles of each item in turn go to its 32 workgroups in ascending order of
+// their work so far (tile t to the workgroup of rank t mod 32).  A pair
+// costs its slabs plus three for its epilogue (two for a zero tile).  The
+// plan needs only the routing, so this runs before dH is ready.
+// Workgroup b = x + 8 l (XCD x, local index l) gets the list
+// list[b * cap ..] of pair codes item * PT + tile, in item order, and its
+// length cnt[b].
+constexpr int kSchedThreads = 512;
+constexpr int kSchedItems = 1536;  // items of one plan (the host checks)
+
+__device__ __forceinline__ void sched_one(const int* __restrict__ header,
+                                          const VarlenItem* __restrict__ items, int PT, int cap,
+                                          int* __restrict__ cnt, int* __restrict__ list) {
+  __shared__ int cost[kSchedItems];
+  __shared__ uint8_t xcd_of[kSchedItems];
+  __shared__ int16_t xl[8][kSchedItems];
+  __shared__ int xn[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ni = min(header[0], kSchedItems);
+  for (int i = tid; i < ni; i += kSchedThreads) {
+    const int r = items[i].ke - items[i].kb;
+    cost[i] = r > 0 ? (r + 63) / 64 + 3 : 2;
+  }
+  __syncthreads();
+  if (wave == 0) {  // items to XCDs: one wave, the eight keys (work << 3 | XCD) in scalar registers
+    int key[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) key[x] = x;
+    for (int i0 = 0; i0 < ni; i0 += 64) {
+      const int cv = i0 + lane < ni ? cost[i0 + lane] * PT : 0;
+      const int m = min(64, ni - i0);
+      int xv = 0;  // lane j: the XCD of item i0 + j
+      for (int j = 0; j < m; ++j) {
+        const int c8 = __builtin_amdgcn_readlane(cv, j) << 3;
+        int best = key[0];  // least work, then lowest XCD
+#pragma unroll
+        for (int x = 1; x < 8; ++x) best = min(best, key[x]);
+        best = __builtin_amdgcn_readfirstlane(best);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) key[x] += key[x] == best ? c8 : 0;
+        xv = lane == j ? (best & 7) : xv;
+      }
+      if (lane < m) xcd_of[i0 + lane] = uint8_t(xv);
+    }
+  }
+  __syncthreads();
+  if (wave < 8) {  // wave x lists XCD x's items in plan order
+    const int x = wave;
+    int n = 0;
+    for (int i0 = 0; i0 < ni; i0 += 64) {
+      const bool mine = i0 + lane < ni && xcd_of[i0 + lane] == x;
+      const uint64_t bal = __ballot(mine);
+      if (mine)
+        xl[x][n + __builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32),
+                                            __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0))] =
+            int16_t(i0 + lane);
+      n += __popcll(bal);
+    }
+    if (lane == 0) xn[x] = n;
+  }
+  __syncthreads();
+  if (wave < 8) {  // wave x: XCD x's pairs; lane l < 32 is workgroup b = x + 8 l
+    const int x = wave, b = x + 8 * lane, nx = xn[x];
+    int key = lane < 32 ? lane : INT_MAX;  // work << 5 | l
+    int c = 0;                             // entries of b's list
+    int* const mine = list + int64_t(b) * cap;
+    for (int k0 = 0; k0 < nx; k0 += 64) {
+      const int iv = k0 + lane < nx ? xl[x][k0 + lane] : 0;
+      const int cv = k0 + lane < nx ? cost[iv] : 0;
+      const int m = min(64, nx - k0);
+      for (int j = 0; j < m; ++j) {
+        const int i = __builtin_amdgcn_readlane(iv, j), ci = __builtin_amdgcn_readlane(cv, j);
+        int r = 0;  // this workgroup's rank by work so far
+#pragma unroll
+        for (int q = 0; q < 32; ++q) r += __builtin_amdgcn_readlane(key, q) < key ? 1 : 0;
+        if (lane < 32) {
+          int nt = 0;
+          for (int t = r; t < PT && c < cap; t += 32, ++nt) mine[c++] = i * PT + t;
+          key += (nt * ci) << 5;
+        }
+      }
+    }
+    if (lane < 32) cnt[b] = c;
+  }
+}
+
+__global__ __launch_bounds__(kSchedThreads) void k_dw_sched(
+    const int* __restrict__ header1, const VarlenItem* __restrict__ items1, int PT1, int cap1,
+    int* __restrict__ cnt1, int* __restrict__ list1, const int* __restrict__ header2,
+    const VarlenItem* __restrict__ items2, int PT2, int cap2, int* __restrict__ cnt2,
+    int* __restrict__ list2) {
+  if (blockIdx.x == 0 && cap1 > 0) sched_one(header1, items1, PT1, cap1, cnt1, list1);
+  if (blockIdx.x == 1 && cap2 > 0) sched_one(header2, items2, PT2, cap2, cnt2, list2);
+}
+
 // out_e = sum over the chunks of a split expert of its fp32 partials, in
 // chunk order (so the result does not depend on which chunk finished first).
 // Work unit u = j * gy + g covers split expert j, elements g*2048 .. +2048
@@ -538,19 +639,24 @@ __device__ __forceinline__ void store_tile_f32(const Accum<Cfg>& acc, float* out
       }
 }
 
-// Zeroes a full weight-gradient tile of an expert that was given no slots
-// (its gradient is exactly zero): whole rows of 16-byte non-temporal
-// stores, without the accumulators and the staging round trip.
-template <class Cfg>
-__device__ __forceinline__ void zero_tile(typename Cfg::T* out, int ld) {
-  constexpr int CPR = Cfg::BN * int(sizeof(typename Cfg::T)) / 16;  // chunks per row
-  static_assert((Cfg::BM * CPR) % Cfg::kThreads == 0, "whole rounds");
+// Zeroes a ROWS x COLS weight-gradient tile of an expert that was given no
+// slots (its gradient is exactly zero): whole rows of 16-byte non-temporal
+// stores by NT threads (thread index tid), without the accumulators and the
+// staging round trip.
+template <class T, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void zero_block(T* out, int ld, int tid) {
+  constexpr int CPR = COLS * int(sizeof(T)) / 16;  // chunks per row
+  static_assert((ROWS * CPR) % NT == 0, "whole rounds");
   const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll 4
-  for (int q = threadIdx.x; q < Cfg::BM * CPR; q += Cfg::kThreads) {
+  for (int q = tid; q < ROWS * CPR; q += NT) {
     char* row = reinterpret_cast<char*>(out + int64_t(q / CPR) * ld);
     __builtin_nontemporal_store(z, reinterpret_cast<u32x4_t*>(row + (q % CPR) * 16));
   }
+}
+template <class Cfg>
+__device__ __forceinline__ void zero_tile(typename Cfg::T* out, int ld) {
+  zero_block<typename Cfg::T, Cfg::BM, Cfg::BN, Cfg::kThreads>(out, ld, threadIdx.x);
 }
 
 // Writes a full weight-gradient tile (rows i0.., columns j0..) through the
@@ -641,6 +747,203 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw2(
     store_tile_f32(acc, partials + (int64_t(it.pslot) * n + i0) * d + j0, d);
 }
 
+// One MN-major operand of a varlen-K tile as a loader wave issues it: COLS
+// columns (from col0) of the source rows of slots s0 .. s0 + BK - 1, where
+// slot s reads row slot_token[s] (GATHER) or row s of a buffer of `rows`
+// rows of `cols` elements.  Loader wave w fills the tile rows 16 w .. 16 w +
+// 15 (BK = 64, four loader waves): lane L of its instruction i fills row
+// 16 w + i RPI + L / CH with the logical 16-byte chunk that the swizzle
+// places at chunk L % CH.  Slots at or past the item's end ke read row
+// `rows`, the first one past the buffer, so the DMA writes zeros to their
+// LDS rows.  The 16 gather indices of a wave's rows are one 64-byte scalar
+// load, issued a slab ahead of their use (fetch, then issue); scalar loads
+// leave the in-order vector-memory counter of the DMA alone.
+template <class Cfg, int COLS, bool GATHER>
+struct SlotOperand {
+  static constexpr int RB = COLS * 2, CH = RB / 16, RPI = 64 / CH;
+  static constexpr int NI = 16 * RB / 1024;  // instructions per wave and slab
+  static_assert(Cfg::BK == 64 && Cfg::NLW == 4, "four loader waves of 16 rows each");
+  static_assert(RPI == 2 || RPI == 4, "rows of 256 or 512 bytes");
+  rsrc_t rs;
+  uint32_t ld;
+  int nrows;
+  uint32_t chunk[NI];  // byte offset, within the source row, of the chunk this lane fetches
+  int w, q;            // loader wave index; this lane's row among an instruction's RPI rows
+  // GATHER: tokens of this wave's 16 slots of the next slab (a vector value,
+  // so that selecting one per lane never becomes an indexed memory access)
+  typedef int v16i_t __attribute__((ext_vector_type(16)));
+  v16i_t t;
+
+  __device__ __forceinline__ void init(const bf16_t* base, int rows, int cols, int w_, int lane) {
+    ld = uint32_t(cols) * 2u;
+    nrows = rows;
+    rs = make_rsrc(base, uint32_t(rows) * ld);
+    w = w_;
+    q = lane / CH;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = 16 * w + i * RPI + q;
+      chunk[i] = uint32_t(((lane % CH) ^ mswz<CH>(k)) << 4);
+    }
+  }
+  // The gather indices of the slab at slot s0 (slot_token holds nslot
+  // entries; near its end each index is clamped to a slot below ke).
+  __device__ __forceinline__ void fetch(int s0, int ke, const int32_t* __restrict__ tok,
+                                        int nslot) {
+    if constexpr (GATHER) {
+      const int b = s0 + 16 * w;
+      v16i_t v;
+      if (b + 16 <= nslot) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = tok[b + j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = tok[min(b + j, ke - 1)];
+      }
+      t = v;
+    }
+  }
+  __device__ __forceinline__ void issue(char* tile, int s0, int ke, int col0) const {
+    const uint32_t cb = uint32_t(col0) * 2u;
+    const v16i_t tv = t;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int slot = s0 + 16 * w + i * RPI + q;
+      int v = slot;
+      if constexpr (GATHER) {
+        v = tv[i * RPI];
+#pragma unroll
+        for (int p = 1; p < RPI; ++p) v = q == p ? tv[i * RPI + p] : v;
+      }
+      const int row = slot < ke ? v : nrows;
+      dma16(rs, uint32_t(row) * ld + cb + chunk[i], tile + (w * NI + i) * 1024);
+    }
+  }
+};
+
+// Weight gradients out_e = A_e^T B_e (varlen-K over the expert's slots) in a
+// persistent launch with loader waves: workgroup b (one per CU, on XCD b % 8)
+// walks the (item, output tile) pairs that k_dw_sched listed for it, pair
+// code c = item * PT + tile.  A and B are MN-major with one row per slot:
+// token rows read through slot_token when GA / GB, else slot rows.  Loader
+// and compute waves pass one barrier per slab and one per tile (items
+// without slots have neither: the compute waves write their zero tiles
+// directly), so the loader waves run up to S - 1 slabs ahead across tile
+// boundaries and the next tile's first slabs land while the compute waves
+// write the last one.  Both roles read the list and the items with scalar
+// loads.  A split item's tile goes to its fp32 partial slab, reduced
+// afterwards.
+template <class Cfg, bool GA, bool GB>
+__global__ __launch_bounds__(Cfg::kThreads) void k_dw_p(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ out,
+    float* __restrict__ partials, const VarlenItem* __restrict__ items,
+    const int* __restrict__ sched_cnt, const int* __restrict__ sched_list, int cap,
+    const int32_t* __restrict__ slot_token, int M, int N, int a_rows, int b_rows, int nslot) {
+  using T = bf16_t;
+  static_assert(Cfg::NPW > 0 && !Cfg::PAIRED, "loader waves, plain columns");
+  constexpr int S = Cfg::STAGES, BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  const int TN = N / BN, PT = (M / BM) * TN;
+  const int ntiles = sched_cnt[blockIdx.x];
+  const int* __restrict__ mine = sched_list + int64_t(blockIdx.x) * cap;
+  // pair k of this workgroup: its item and the output tile's first row / column
+  auto pair = [&](int k, VarlenItem& it, int& i0, int& j0) {
+    const int c = mine[k], tile = c % PT;
+    it = items[c / PT];
+    i0 = (tile / TN) * BM;
+    j0 = (tile % TN) * BN;
+  };
+
+  if (Cfg::loads(wave_id())) {
+    const int lw = Cfg::loader_index(wave_id()), lane = threadIdx.x & 63;
+    SlotOperand<Cfg, BM, GA> oa;
+    oa.init(A, a_rows, M, lw, lane);
+    SlotOperand<Cfg, BN, GB> ob;
+    ob.init(B, b_rows, N, lw, lane);
+    constexpr int NI = SlotOperand<Cfg, BM, GA>::NI + SlotOperand<Cfg, BN, GB>::NI;
+    static_assert(S >= 2 && S <= 4 && NI * (S - 2) < 64, "pipeline depth");
+    // The issue side walks the same stream of slabs ahead of the barriers:
+    // pair ki, its slab si of ns.
+    int ki = -1, si = 0, ns = 0, kb = 0, ke = 0, i0 = 0, j0 = 0;
+    auto next_pair = [&]() {  // the next pair with slots (ki == ntiles at the end)
+      while (++ki < ntiles) {
+        VarlenItem it;
+        pair(ki, it, i0, j0);
+        kb = it.kb;
+        ke = it.ke;
+        if (ke > kb) {
+          ns = (ke - kb + BK - 1) / BK;
+          si = 0;
+          return;
+        }
+      }
+    };
+    auto fetch = [&]() {  // the gather indices of the next slab to issue
+      if (ki >= ntiles) return;
+      oa.fetch(kb + si * BK, ke, slot_token, nslot);
+      ob.fetch(kb + si * BK, ke, slot_token, nslot);
+    };
+    next_pair();
+    fetch();
+    int issued = 0;
+    auto issue = [&]() {
+      if (ki >= ntiles) return;
+      char* sp = lds + (issued % S) * Cfg::STAGE_BYTES;
+      const int s0 = kb + si * BK;
+      oa.issue(sp, s0, ke, i0);
+      ob.issue(sp + Cfg::A_BYTES, s0, ke, j0);
+      ++issued;
+      if (++si == ns) next_pair();
+      fetch();
+    };
+    for (int p = 0; p < S - 1; ++p) issue();
+    int g = 0;  // slabs consumed
+    for (int k = 0; k < ntiles; ++k) {
+      VarlenItem it;
+      int pi, pj;
+      pair(k, it, pi, pj);
+      const int kbk = it.kb, kek = it.ke;
+      if (kek == kbk) continue;
+      const int nsk = (kek - kbk + BK - 1) / BK;
+      for (int j = 0; j < nsk; ++j, ++g) {
+        wait_slab<S, NI>(issued - 1 - g);  // slab g landed; later ones may fly
+        barrier();
+        issue();  // into the stage of slab g - 1, which every compute wave is done with
+      }
+      barrier();  // the compute waves write tile k
+    }
+    return;
+  }
+  Accum<Cfg> acc;
+  int g = 0;
+  for (int k = 0; k < ntiles; ++k) {
+    VarlenItem t;
+    int i0, j0;
+    pair(k, t, i0, j0);
+    if (t.ke == t.kb) {  // an expert without slots (never split)
+      zero_block<T, BM, BN, 64 * Cfg::NW>(out + (int64_t(t.e) * M + i0) * N + j0, N,
+                                          threadIdx.x);
+      continue;
+    }
+    const int ns = (t.ke - t.kb + BK - 1) / BK;
+    acc.init();
+    for (int j = 0; j < ns; ++j, ++g) {
+      barrier();
+      const char* cur = lds + (g % S) * Cfg::STAGE_BYTES;
+      acc.template slab<false, false>(cur, cur + Cfg::A_BYTES);
+    }
+    barrier();  // every compute wave is done with the last slab's stage
+    if (t.pslot < 0) {
+      static_assert(RowStage<T, Cfg::WTN>::BYTES * Cfg::NW <= Cfg::STAGE_BYTES, "staging fits");
+      T* o = out + (int64_t(t.e) * M + i0) * N + j0;
+      store_acc_staged(acc, lds + ((g - 1) % S) * Cfg::STAGE_BYTES,
+                       [&](int r) -> T* { return o + int64_t(r) * N; });
+    } else {
+      store_tile_f32(acc, partials + (int64_t(t.pslot) * M + i0) * N + j0, N);
+    }
+  }
+}
+
 template <class Cfg>
 void dh_launch(const LayerArgs& a, const void* dO, const void* W2, const void* H, void* dH,
                void* As, float* dS, hipStream_t st) {
@@ -681,44 +984,12 @@ void dxt_launch(const LayerArgs& a, const void* dH, const void* W1, void* dXt, h
                      a.expert_offsets, a.totals, a.d, a.n, int(a.slot_cap));
 }
 
-// Tile configurations of the two weight-gradient kernels; f(CfgTag<Cfg>{})
-// is called with the one the problem uses (the launchers and the workspace
-// sizing share this choice).
-template <class C>
-struct CfgTag {
-  using type = C;
-};
-
-template <class F>
-void dw1_cfg(bool f32, int d, int n, F&& f) {
-  const int n2 = 2 * n;
-  if (f32) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
-  else if (d % 256 == 0 && n2 % 256 == 0) f(CfgTag<GradSquare>{});
-  else if (n2 % 256 == 0) f(CfgTag<GradTall>{});
-  else f(CfgTag<GradSmall>{});
-}
-
-template <class F>
-void dw2_cfg(bool f32, int d, int n, F&& f) {
-  if (f32) {
-    if (n % 128 == 0) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
-    else f(CfgTag<TileCfg<float, 64, 128, 2, 2, 3>>{});
-  } else if (n % 256 == 0 && d % 256 == 0) {
-    f(CfgTag<GradSquare>{});
-  } else if (n % 128 == 0 && d % 256 == 0) {
-    f(CfgTag<GradTall>{});
-  } else if (n % 128 == 0) {
-    f(CfgTag<GradSmall>{});
-  } else {
-    f(CfgTag<TileCfg<bf16_t, 64, 128, 2, 2, 3>>{});
-  }
-}
-
 // Chunking of one varlen-K kernel: PT output tiles per expert, chunks of kc
 // rows, and the capacities of its plan.
 struct VarlenDims {
   int PT, kc, max_items, max_split;
   int64_t mn;  // elements of one expert's gradient matrix
+  int cap;     // persistent kernel: capacity of each workgroup's pair list (0: per-tile kernel)
 };
 
 // kc: one CU's fair share of the kernel's work (in rows of a tile), so that
@@ -737,23 +1008,71 @@ inline VarlenDims varlen_dims(int64_t slot_cap, int E, int PT, int BK, int64_t m
   v.max_items = int(E + chunks);  // every expert is one item, plus extra chunks
   v.max_split = int(2 * chunks);  // a split expert has r > kc rows and < 2 r / kc chunks
   v.mn = mn;
+  v.cap = 0;
   return v;
+}
+
+// Tile configurations of the two weight-gradient kernels; f(CfgTag<Cfg>{})
+// is called with the one the problem uses (the launchers and the workspace
+// sizing share this choice).
+template <class C>
+struct CfgTag {
+  using type = C;
+};
+
+// The persistent kernel takes the 128 x 256 tiles with loader waves when its
+// schedule can list every item of the plan.
+inline bool split_fits(int64_t slot_cap, int E, int PT) {
+  return varlen_dims(slot_cap, E, PT, GradSplit::BK, 0).max_items <= kSchedItems;
+}
+// A workgroup gets at most ceil(PT / 32) tiles of each item.
+inline int sched_cap(const VarlenDims& v) { return v.max_items * ((v.PT + 31) / 32); }
+
+template <class F>
+void dw1_cfg(bool f32, int d, int n, int E, int64_t slot_cap, F&& f) {
+  const int n2 = 2 * n;
+  if (f32) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
+  else if (d % 128 == 0 && n2 % 256 == 0 && split_fits(slot_cap, E, (d / 128) * (n2 / 256)))
+    f(CfgTag<GradSplit>{});
+  else if (d % 256 == 0 && n2 % 256 == 0) f(CfgTag<GradSquare>{});
+  else if (n2 % 256 == 0) f(CfgTag<GradTall>{});
+  else f(CfgTag<GradSmall>{});
+}
+
+template <class F>
+void dw2_cfg(bool f32, int d, int n, int E, int64_t slot_cap, F&& f) {
+  if (f32) {
+    if (n % 128 == 0) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
+    else f(CfgTag<TileCfg<float, 64, 128, 2, 2, 3>>{});
+  } else if (n % 128 == 0 && d % 256 == 0 && split_fits(slot_cap, E, (n / 128) * (d / 256))) {
+    f(CfgTag<GradSplit>{});
+  } else if (n % 256 == 0 && d % 256 == 0) {
+    f(CfgTag<GradSquare>{});
+  } else if (n % 128 == 0 && d % 256 == 0) {
+    f(CfgTag<GradTall>{});
+  } else if (n % 128 == 0) {
+    f(CfgTag<GradSmall>{});
+  } else {
+    f(CfgTag<TileCfg<bf16_t, 64, 128, 2, 2, 3>>{});
+  }
 }
 
 VarlenDims dw1_dims(bool f32, int d, int n, int E, int64_t slot_cap) {
   VarlenDims v{};
-  dw1_cfg(f32, d, n, [&](auto tag) {
+  dw1_cfg(f32, d, n, E, slot_cap, [&](auto tag) {
     using Cfg = typename decltype(tag)::type;
     v = varlen_dims(slot_cap, E, (d / Cfg::BM) * (2 * n / Cfg::BN), Cfg::BK, int64_t(d) * 2 * n);
+    if constexpr (Cfg::NPW > 0) v.cap = sched_cap(v);
   });
   return v;
 }
 
 VarlenDims dw2_dims(bool f32, int d, int n, int E, int64_t slot_cap) {
   VarlenDims v{};
-  dw2_cfg(f32, d, n, [&](auto tag) {
+  dw2_cfg(f32, d, n, E, slot_cap, [&](auto tag) {
     using Cfg = typename decltype(tag)::type;
     v = varlen_dims(slot_cap, E, (n / Cfg::BM) * (d / Cfg::BN), Cfg::BK, int64_t(n) * d);
+    if constexpr (Cfg::NPW > 0) v.cap = sched_cap(v);
   });
   return v;
 }
@@ -761,7 +1080,7 @@ VarlenDims dw2_dims(bool f32, int d, int n, int E, int64_t slot_cap) {
 // Workspace of the weight-gradient phase: two plans, then the fp32 partial
 // slabs (shared: dW2 runs after dW1's reduction).
 struct VarlenWs {
-  size_t hdr1, items1, splits1, hdr2, items2, splits2, partials, total;
+  size_t hdr1, items1, splits1, hdr2, items2, splits2, cnt1, list1, cnt2, list2, partials, total;
   static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
   static VarlenWs make(const VarlenDims& v1, const VarlenDims& v2, int E) {
     VarlenWs w;
@@ -772,6 +1091,10 @@ struct VarlenWs {
     w.hdr2 = o; o = align(o + 16);
     w.items2 = o; o = align(o + size_t(v2.max_items) * sizeof(VarlenItem));
     w.splits2 = o; o = align(o + size_t(E) * sizeof(VarlenSplit));
+    w.cnt1 = o; o = align(o + (v1.cap > 0 ? kNumCUs * sizeof(int) : 0));
+    w.list1 = o; o = align(o + size_t(kNumCUs) * size_t(v1.cap) * sizeof(int));
+    w.cnt2 = o; o = align(o + (v2.cap > 0 ? kNumCUs * sizeof(int) : 0));
+    w.list2 = o; o = align(o + size_t(kNumCUs) * size_t(v2.cap) * sizeof(int));
     w.partials = o;
     o += std::max(size_t(v1.max_split) * size_t(v1.mn), size_t(v2.max_split) * size_t(v2.mn)) * 4;
     w.total = align(o);
@@ -837,8 +1160,7 @@ size_t varlen_ws_bytes(bool f32, int d, int n, int E, int64_t slot_cap) {
       .total;
 }
 
-hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1, void* vws,
-                      hipStream_t st) {
+hipError_t launch_dw_plan(const LayerArgs& a, void* vws, hipStream_t st) {
   const VarlenDims v1 = dw1_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
   const VarlenDims v2 = dw2_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
   const VarlenWs L = VarlenWs::make(v1, v2, a.E);
@@ -847,19 +1169,43 @@ hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* d
   int* hdr2 = reinterpret_cast<int*>(w + L.hdr2);
   auto* items1 = reinterpret_cast<VarlenItem*>(w + L.items1);
   auto* items2 = reinterpret_cast<VarlenItem*>(w + L.items2);
-  auto* splits1 = reinterpret_cast<VarlenSplit*>(w + L.splits1);
-  auto* splits2 = reinterpret_cast<VarlenSplit*>(w + L.splits2);
-  float* partials = reinterpret_cast<float*>(w + L.partials);
   hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(kPlanThreads), 0, st, a.expert_offsets,
-                     a.expert_order, a.E, v1.kc, v2.kc, hdr1, items1, splits1, hdr2, items2,
-                     splits2);
-  dw1_cfg(a.f32, a.d, a.n, [&](auto tag) {
+                     a.expert_order, a.E, v1.kc, v2.kc, hdr1, items1,
+                     reinterpret_cast<VarlenSplit*>(w + L.splits1), hdr2, items2,
+                     reinterpret_cast<VarlenSplit*>(w + L.splits2));
+  if (v1.cap > 0 || v2.cap > 0)
+    hipLaunchKernelGGL(k_dw_sched, dim3(2), dim3(kSchedThreads), 0, st, hdr1, items1, v1.PT,
+                       v1.cap, reinterpret_cast<int*>(w + L.cnt1), reinterpret_cast<int*>(w + L.list1),
+                       hdr2, items2, v2.PT, v2.cap, reinterpret_cast<int*>(w + L.cnt2),
+                       reinterpret_cast<int*>(w + L.list2));
+  return hipGetLastError();
+}
+
+hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1, void* vws,
+                      hipStream_t st) {
+  const VarlenDims v1 = dw1_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
+  const VarlenDims v2 = dw2_dims(a.f32, a.d, a.n, a.E, a.slot_cap);
+  const VarlenWs L = VarlenWs::make(v1, v2, a.E);
+  char* w = static_cast<char*>(vws);
+  int* hdr1 = reinterpret_cast<int*>(w + L.hdr1);
+  auto* items1 = reinterpret_cast<VarlenItem*>(w + L.items1);
+  auto* splits1 = reinterpret_cast<VarlenSplit*>(w + L.splits1);
+  float* partials = reinterpret_cast<float*>(w + L.partials);
+  dw1_cfg(a.f32, a.d, a.n, a.E, a.slot_cap, [&](auto tag) {
     using Cfg = typename decltype(tag)::type;
     using T = typename Cfg::T;
-    hipLaunchKernelGGL((k_dw1<Cfg>), dim3(unsigned(8 * cdiv(v1.max_items, 8) * v1.PT)),
-                       dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
-                       static_cast<const T*>(dH), static_cast<T*>(dW1), partials, hdr1, items1,
-                       a.slot_token, a.d, a.n, a.T, int(a.slot_cap));
+    if constexpr (Cfg::NPW > 0)
+      hipLaunchKernelGGL((k_dw_p<Cfg, true, false>), dim3(kNumCUs), dim3(Cfg::kThreads), 0, st,
+                         static_cast<const T*>(X), static_cast<const T*>(dH),
+                         static_cast<T*>(dW1), partials, items1,
+                         reinterpret_cast<const int*>(w + L.cnt1),
+                         reinterpret_cast<const int*>(w + L.list1), v1.cap, a.slot_token, a.d,
+                         2 * a.n, a.T, int(a.slot_cap), int(a.slot_cap));
+    else
+      hipLaunchKernelGGL((k_dw1<Cfg>), dim3(unsigned(8 * cdiv(v1.max_items, 8) * v1.PT)),
+                         dim3(Cfg::kThreads), 0, st, static_cast<const T*>(X),
+                         static_cast<const T*>(dH), static_cast<T*>(dW1), partials, hdr1, items1,
+                         a.slot_token, a.d, a.n, a.T, int(a.slot_cap));
     reduce_launch<T>(hdr1, splits1, partials, dW1, v1, st);
   });
   return hipGetLastError();
@@ -875,13 +1221,21 @@ hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* 
   auto* items2 = reinterpret_cast<VarlenItem*>(w + L.items2);
   auto* splits2 = reinterpret_cast<VarlenSplit*>(w + L.splits2);
   float* partials = reinterpret_cast<float*>(w + L.partials);
-  dw2_cfg(a.f32, a.d, a.n, [&](auto tag) {
+  dw2_cfg(a.f32, a.d, a.n, a.E, a.slot_cap, [&](auto tag) {
     using Cfg = typename decltype(tag)::type;
     using T = typename Cfg::T;
-    hipLaunchKernelGGL((k_dw2<Cfg>), dim3(unsigned(8 * cdiv(v2.max_items, 8) * v2.PT)),
-                       dim3(Cfg::kThreads), 0, st, static_cast<const T*>(As),
-                       static_cast<const T*>(dO), static_cast<T*>(dW2), partials, hdr2, items2,
-                       a.slot_token, a.d, a.n, a.T, int(a.slot_cap));
+    if constexpr (Cfg::NPW > 0)
+      hipLaunchKernelGGL((k_dw_p<Cfg, false, true>), dim3(kNumCUs), dim3(Cfg::kThreads), 0, st,
+                         static_cast<const T*>(As), static_cast<const T*>(dO),
+                         static_cast<T*>(dW2), partials, items2,
+                         reinterpret_cast<const int*>(w + L.cnt2),
+                         reinterpret_cast<const int*>(w + L.list2), v2.cap, a.slot_token, a.n,
+                         a.d, int(a.slot_cap), a.T, int(a.slot_cap));
+    else
+      hipLaunchKernelGGL((k_dw2<Cfg>), dim3(unsigned(8 * cdiv(v2.max_items, 8) * v2.PT)),
+                         dim3(Cfg::kThreads), 0, st, static_cast<const T*>(As),
+                         static_cast<const T*>(dO), static_cast<T*>(dW2), partials, hdr2, items2,
+                         a.slot_token, a.d, a.n, a.T, int(a.slot_cap));
     reduce_launch<T>(hdr2, splits2, partials, dW2, v2, st);
   });
   return hipGetLastError();

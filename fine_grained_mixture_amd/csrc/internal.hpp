@@ -59,9 +59,11 @@ hipError_t launch_dh(const LayerArgs& a, const void* dO, const void* W2, const v
 hipError_t launch_dxt(const LayerArgs& a, const void* dH, const void* W1, void* dXt,
                       hipStream_t st);
 // Varlen-K weight gradients.  `vws` is the weight-gradient workspace of
-// varlen_ws_bytes() bytes (chunk plans and fp32 partial sums); launch_dw1
-// also writes both plans, so it must run first.
+// varlen_ws_bytes() bytes (chunk plans, the persistent kernels' schedules
+// and fp32 partial sums).  launch_dw_plan writes the plans and schedules
+// from the routing alone and must run before launch_dw1 and launch_dw2.
 size_t varlen_ws_bytes(bool f32, int d, int n, int E, int64_t slot_cap);
+hipError_t launch_dw_plan(const LayerArgs& a, void* vws, hipStream_t st);
 hipError_t launch_dw1(const LayerArgs& a, const void* X, const void* dH, void* dW1, void* vws,
                       hipStream_t st);
 hipError_t launch_dw2(const LayerArgs& a, const void* As, const void* dO, void* dW2, void* vws,

@@ -109,7 +109,7 @@ void sizes_of(const moe_problem* p, moe_sizes_t* s) {
 constexpr int kMaxDevices = 64;
 struct SideStream {
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, ready = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
@@ -133,18 +133,21 @@ hipError_t side_stream(hipStream_t caller, SideStream** out) {
   SideStream& s = g_side[dev];
   if (!s.stream) {
     hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
+    hipEvent_t f = nullptr, r = nullptr, j = nullptr;
     e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
     if (e != hipSuccess) {
       if (j) (void)hipEventDestroy(j);
+      if (r) (void)hipEventDestroy(r);
       if (f) (void)hipEventDestroy(f);
       if (st) (void)hipStreamDestroy(st);
       return e;
     }
     s.stream = st;
     s.fork = f;
+    s.ready = r;
     s.join = j;
   }
   *out = &s;
@@ -364,37 +367,49 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
     if (side_stream(sm, &side) != hipSuccess) return MOE_ERR_HIP;
     if (!side) lock.unlock();
   }
-  tr.mark(sm, 0);
-  hipError_t e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  tr.mark(sm, 1);
   if (!side) {
     // traced (or no side stream): every kernel in order on the caller's
     // stream, so that each segment between two events times one kernel
+    // (the weight-gradient plans count with dW1)
+    tr.mark(sm, 0);
+    hipError_t e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    tr.mark(sm, 1);
     e = moe::launch_dxt(a, dH, W1, dXt, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 2);
     e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 3);
-    e = moe::launch_dw1(a, X, dH, dW1, vws, sm);
+    e = moe::launch_dw_plan(a, vws, sm);
+    if (e == hipSuccess) e = moe::launch_dw1(a, X, dH, dW1, vws, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 4);
     e = moe::launch_dw2(a, As, dO, dW2, vws, sm);
     tr.mark(sm, 5);
     return hip_status(e);
   }
-  // Untraced: dX~ and its aggregation on the caller's stream, and beside
-  // them dW1 then dW2 on the side stream.  Both chains need only dH / s*A,
-  // and neither writes what the other reads.  Running them together keeps
-  // the CUs out of step: one kernel's tiles store their outputs while the
-  // other's stream operands, instead of every CU storing at once.
-  e = hipEventRecord(side->fork, sm);
+  // Untraced: the weight-gradient plans, which need only the routing, run
+  // on the side stream beside dH.  Then dX~ and its aggregation run on the
+  // caller's stream and, beside them, dW1 then dW2 on the side stream.  Both
+  // chains need only dH / s*A, and neither writes what the other reads.
+  // Running them together keeps the CUs out of step: one kernel's tiles
+  // store their outputs while the other's stream operands, instead of every
+  // CU storing at once.
+  hipError_t e = hipEventRecord(side->fork, sm);
   if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  hipError_t e_main = moe::launch_dxt(a, dH, W1, dXt, sm);
+  hipError_t e_side = moe::launch_dw_plan(a, vws, side->stream);
+  hipError_t e_main = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
+  if (e_main == hipSuccess) e_main = hipEventRecord(side->ready, sm);
+  // the side stream goes on only once it waits for dH
+  if (e_main == hipSuccess && e_side == hipSuccess)
+    e_side = hipStreamWaitEvent(side->stream, side->ready, 0);
+  else if (e_side == hipSuccess)
+    e_side = hipErrorNotReady;
+  if (e_main == hipSuccess) e_main = moe::launch_dxt(a, dH, W1, dXt, sm);
   if (e_main == hipSuccess) e_main = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
-  hipError_t e_side = moe::launch_dw1(a, X, dH, dW1, vws, side->stream);
+  if (e_side == hipSuccess) e_side = moe::launch_dw1(a, X, dH, dW1, vws, side->stream);
   if (e_side == hipSuccess) e_side = moe::launch_dw2(a, As, dO, dW2, vws, side->stream);
   // join whatever was enqueued, so the caller's stream (or its capture) ends
   // after both chains even on an error

@@ -9,6 +9,8 @@
 //   RowsSplit           the same, 128 x 256, four compute and four loader
 //                       waves, in persistent launches (one workgroup per CU)
 //   DhWide              dH for n = 256: 128 slot rows x all 256 columns
+//   GradSplit           dW1 / dW2 (varlen-K), 128 x 256 with loader waves,
+//                       in persistent launches
 //   GradSquare/Tall/Small  dW1 / dW2 (varlen-K): 256x256 / 128x256 / 128x128
 #pragma once
 
@@ -26,6 +28,9 @@ using RowsSplit = TileCfg<bf16_t, 128, 256, 2, 2, 3, 128, false, 4>;
 // slabs of 16 KB, two per stage, in a three-stage ring
 using RowsReg = TileCfg<bf16_t, 128, 128, 4, 1, 3, 128, false, 4>;
 using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
+// dW1 / dW2 in persistent launches: 128 x 256, four compute and four loader
+// waves, three 48 KB stages (the shape of RowsSplit, MN-major operands)
+using GradSplit = TileCfg<bf16_t, 128, 256, 2, 2, 3, 128, false, 4>;
 using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 
 using DhWide512 = TileCfg<bf16_t, 64, 512, 1, 4, 2, 128>;  // dH for n = 512 (one wave per SIMD)
