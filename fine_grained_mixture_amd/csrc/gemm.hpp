@@ -66,9 +66,9 @@ struct TileCfg {
   static constexpr int NLW = NPW > 0 ? NPW : NW;  // waves that issue DMA
   static constexpr int kThreads = 64 * (NW + NPW);
   static_assert(NW == 4 || NW == 8, "four or eight compute waves per workgroup");
-  static_assert(NPW == 0 || (NW == 4 && NPW == 4), "four loader waves beside four compute waves");
-  // Wave w's roles.  Waves w and w + 4 share a SIMD, so with loader waves
-  // every SIMD runs one compute wave and one loader wave.
+  static_assert(NPW == 0 || NPW == 4, "four loader waves beside four or eight compute waves");
+  // Wave w's roles.  Waves w, w + 4, w + 8 share a SIMD, so with loader
+  // waves every SIMD runs one or two compute waves and one loader wave.
   __device__ static constexpr bool loads(int w) { return NPW == 0 || w >= NW; }
   __device__ static constexpr int loader_index(int w) { return NPW == 0 ? w : w - NW; }
   static constexpr int BK = KB / int(sizeof(T));  // k-values per slab
@@ -405,6 +405,19 @@ struct Accum {
       // keep those reads ahead of this chunk's MFMAs
       __builtin_amdgcn_sched_barrier(0);
       mma(fa[kc & 1], fb[kc & 1]);
+    }
+  }
+
+  // One slab with a single set of fragment registers: chunk kc's reads,
+  // then its MFMAs.  For tiles whose accumulators leave no room for a
+  // second set; the SIMD's other compute wave covers the read latency.
+  template <bool AK, bool BKM>
+  __device__ __forceinline__ void slab1(const char* As, const char* Bs) {
+#pragma unroll
+    for (int kc = 0; kc < Cfg::KCH; ++kc) {
+      Oct<T> fa[Cfg::MB], fb[Cfg::NB];
+      frags<AK, BKM>(fa, fb, As, Bs, kc);
+      mma(fa, fb);
     }
   }
 

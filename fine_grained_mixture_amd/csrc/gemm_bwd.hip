@@ -930,7 +930,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dw_p(
     for (int j = 0; j < ns; ++j, ++g) {
       barrier();
       const char* cur = lds + (g % S) * Cfg::STAGE_BYTES;
-      acc.template slab<false, false>(cur, cur + Cfg::A_BYTES);
+      if constexpr (Cfg::NW == 8) acc.template slab1<false, false>(cur, cur + Cfg::A_BYTES);
+      else acc.template slab<false, false>(cur, cur + Cfg::A_BYTES);
     }
     barrier();  // every compute wave is done with the last slab's stage
     if (t.pslot < 0) {
@@ -1020,10 +1021,13 @@ struct CfgTag {
   using type = C;
 };
 
-// The persistent kernel takes the 128 x 256 tiles with loader waves when its
-// schedule can list every item of the plan.
-inline bool split_fits(int64_t slot_cap, int E, int PT) {
-  return varlen_dims(slot_cap, E, PT, GradSplit::BK, 0).max_items <= kSchedItems;
+// The persistent kernel takes tile Cfg for an M x N gradient when the tile
+// divides it and the schedule can list every item of the plan.
+template <class Cfg>
+bool split_fits(int M, int N, int64_t slot_cap, int E) {
+  if (M % Cfg::BM != 0 || N % Cfg::BN != 0) return false;
+  const int PT = (M / Cfg::BM) * (N / Cfg::BN);
+  return varlen_dims(slot_cap, E, PT, Cfg::BK, 0).max_items <= kSchedItems;
 }
 // A workgroup gets at most ceil(PT / 32) tiles of each item.
 inline int sched_cap(const VarlenDims& v) { return v.max_items * ((v.PT + 31) / 32); }
@@ -1032,8 +1036,8 @@ template <class F>
 void dw1_cfg(bool f32, int d, int n, int E, int64_t slot_cap, F&& f) {
   const int n2 = 2 * n;
   if (f32) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
-  else if (d % 128 == 0 && n2 % 256 == 0 && split_fits(slot_cap, E, (d / 128) * (n2 / 256)))
-    f(CfgTag<GradSplit>{});
+  else if (split_fits<GradSplit256>(d, n2, slot_cap, E)) f(CfgTag<GradSplit256>{});
+  else if (split_fits<GradSplit>(d, n2, slot_cap, E)) f(CfgTag<GradSplit>{});
   else if (d % 256 == 0 && n2 % 256 == 0) f(CfgTag<GradSquare>{});
   else if (n2 % 256 == 0) f(CfgTag<GradTall>{});
   else f(CfgTag<GradSmall>{});
@@ -1044,7 +1048,9 @@ void dw2_cfg(bool f32, int d, int n, int E, int64_t slot_cap, F&& f) {
   if (f32) {
     if (n % 128 == 0) f(CfgTag<TileCfg<float, 128, 128, 2, 2, 3>>{});
     else f(CfgTag<TileCfg<float, 64, 128, 2, 2, 3>>{});
-  } else if (n % 128 == 0 && d % 256 == 0 && split_fits(slot_cap, E, (n / 128) * (d / 256))) {
+  } else if (split_fits<GradSplit256>(n, d, slot_cap, E)) {
+    f(CfgTag<GradSplit256>{});
+  } else if (split_fits<GradSplit>(n, d, slot_cap, E)) {
     f(CfgTag<GradSplit>{});
   } else if (n % 256 == 0 && d % 256 == 0) {
     f(CfgTag<GradSquare>{});

@@ -9,8 +9,8 @@
 //   RowsSplit           the same, 128 x 256, four compute and four loader
 //                       waves, in persistent launches (one workgroup per CU)
 //   DhWide              dH for n = 256: 128 slot rows x all 256 columns
-//   GradSplit           dW1 / dW2 (varlen-K), 128 x 256 with loader waves,
-//                       in persistent launches
+//   GradSplit256/Split  dW1 / dW2 (varlen-K), 256 x 256 / 128 x 256 with
+//                       loader waves, in persistent launches
 //   GradSquare/Tall/Small  dW1 / dW2 (varlen-K): 256x256 / 128x256 / 128x128
 #pragma once
 
@@ -28,8 +28,10 @@ using RowsSplit = TileCfg<bf16_t, 128, 256, 2, 2, 3, 128, false, 4>;
 // slabs of 16 KB, two per stage, in a three-stage ring
 using RowsReg = TileCfg<bf16_t, 128, 128, 4, 1, 3, 128, false, 4>;
 using GradSquare = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128>;
-// dW1 / dW2 in persistent launches: 128 x 256, four compute and four loader
-// waves, three 48 KB stages (the shape of RowsSplit, MN-major operands)
+// dW1 / dW2 in persistent launches: 256 x 256 with eight compute and four
+// loader waves (three per SIMD, so 168 registers each) in two 64 KB stages;
+// else 128 x 256 with four of each in three 48 KB stages
+using GradSplit256 = TileCfg<bf16_t, 256, 256, 2, 4, 2, 128, false, 4>;
 using GradSplit = TileCfg<bf16_t, 128, 256, 2, 2, 3, 128, false, 4>;
 using DhWide = TileCfg<bf16_t, 128, 256, 2, 4, 3, 128>;
 
