@@ -549,6 +549,29 @@ struct PersistentShare {
   }
 };
 
+// A 16-byte tile descriptor from LDS for a wave that has DMA into LDS in
+// flight.  The compiler cannot tell that the descriptor table is never a DMA
+// destination, so a plain LDS read would first wait for every DMA of the
+// wave; this read waits only for itself.  Its fields are made wave-uniform
+// (they are: every lane reads the same entry), so buffer descriptors built
+// from them stay in scalar registers.
+template <class Tile>
+__device__ __forceinline__ Tile lds_tile(const Tile* p) {
+  static_assert(sizeof(Tile) == 16, "16-byte descriptors");
+  typedef unsigned u32x4v_t __attribute__((ext_vector_type(4)));
+  const uint32_t a =
+      uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+  u32x4v_t v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  const uint32_t w[4] = {uint32_t(__builtin_amdgcn_readfirstlane(int(v.x))),
+                         uint32_t(__builtin_amdgcn_readfirstlane(int(v.y))),
+                         uint32_t(__builtin_amdgcn_readfirstlane(int(v.z))),
+                         uint32_t(__builtin_amdgcn_readfirstlane(int(v.w)))};
+  Tile t;
+  __builtin_memcpy(&t, w, sizeof(t));
+  return t;
+}
+
 // The slab pipeline of a persistent workgroup with loader waves: its ntiles
 // tiles (each of nslabs >= S - 1 slabs) form one stream of slabs.  The loader
 // waves issue and wait for every DMA and run ahead across tile boundaries,
@@ -559,8 +582,8 @@ struct PersistentShare {
 // the loader waves that stage (g - 1) % S is free; the barrier after a
 // tile's last slab frees that slab's stage for the epilogue's staging, until
 // the next slab's barrier.
-//   describe(k)          descriptor of tile k (a trivially copyable struct);
-//                        all are read once into `table` (LDS) at the start
+//   describe(k)          descriptor of tile k (a 16-byte trivially copyable
+//                        struct); all are read once into `table` (LDS)
 //   loaders(desc)        the LoadPair of a tile (called in loader waves)
 //   epilogue(desc, acc, stage)  writes a finished tile, staging through the
 //                        STAGE_BYTES at `stage` (called in compute waves)
@@ -574,8 +597,8 @@ __device__ __forceinline__ void persistent_split(char* lds, Tile* table, int nti
   __syncthreads();
   const int G = ntiles * nslabs;  // slabs in the stream
   if (Cfg::loads(wave_id())) {
-    auto cur = loaders(table[0]);
-    auto nxt = loaders(table[ntiles > 1 ? 1 : 0]);
+    auto cur = loaders(lds_tile(table));
+    auto nxt = loaders(lds_tile(table + (ntiles > 1 ? 1 : 0)));
     using LP = decltype(cur);
     constexpr int NI = decltype(cur.la)::NI + decltype(cur.lb)::NI;
     static_assert(S >= 2 && S <= 4 && NI * (S - 2) < 64, "pipeline depth");
@@ -601,7 +624,7 @@ __device__ __forceinline__ void persistent_split(char* lds, Tile* table, int nti
       barrier();  // the compute waves write tile k
       if (k + 1 < ntiles) {
         cur = nxt;
-        if (k + 2 < ntiles) nxt = loaders(table[k + 2]);
+        if (k + 2 < ntiles) nxt = loaders(lds_tile(table + k + 2));
       }
     }
     return;
@@ -613,7 +636,8 @@ __device__ __forceinline__ void persistent_split(char* lds, Tile* table, int nti
     for (int j = 0; j < nslabs; ++j) {
       barrier();
       const char* cur = lds + ((k * nslabs + j) % S) * Cfg::STAGE_BYTES;
-      acc.template slab<AK, BKM>(cur, cur + Cfg::A_BYTES);
+      if constexpr (Cfg::NW == 8) acc.template slab1<AK, BKM>(cur, cur + Cfg::A_BYTES);
+      else acc.template slab<AK, BKM>(cur, cur + Cfg::A_BYTES);
     }
     barrier();  // every compute wave is done with the last slab's stage
     epilogue(desc, acc, lds + ((k * nslabs + nslabs - 1) % S) * Cfg::STAGE_BYTES);

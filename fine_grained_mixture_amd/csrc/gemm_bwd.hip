@@ -244,7 +244,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_dxt_p(
     int e, row0, rend, j0;
   };
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
-  __shared__ Tile table[kPersistentTiles];
+  __shared__ __attribute__((aligned(16))) Tile table[kPersistentTiles];
   constexpr int BN = Cfg::BN;
   const int NT = d / BN, n2 = 2 * n;
   const PersistentShare ps = PersistentShare::make(totals[1] * NT);

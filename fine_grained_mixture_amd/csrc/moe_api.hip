@@ -368,25 +368,26 @@ int moe_bwd(const moe_problem* p, const void* dO, const void* X, const void* H, 
     if (!side) lock.unlock();
   }
   if (!side) {
-    // traced (or no side stream): every kernel in order on the caller's
-    // stream, so that each segment between two events times one kernel
-    // (the weight-gradient plans count with dW1)
+    // traced (or no side stream): every step in order on the caller's
+    // stream, so that each segment between two events times one step
     tr.mark(sm, 0);
-    hipError_t e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
+    hipError_t e = moe::launch_dw_plan(a, vws, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 1);
-    e = moe::launch_dxt(a, dH, W1, dXt, sm);
+    e = moe::launch_dh(a, dO, W2, H, dH, As, dS, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 2);
-    e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
+    e = moe::launch_dxt(a, dH, W1, dXt, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 3);
-    e = moe::launch_dw_plan(a, vws, sm);
-    if (e == hipSuccess) e = moe::launch_dw1(a, X, dH, dW1, vws, sm);
+    e = moe::launch_aggregate(a, dXt, false, dX, a.d, sm);
     if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 4);
-    e = moe::launch_dw2(a, As, dO, dW2, vws, sm);
+    e = moe::launch_dw1(a, X, dH, dW1, vws, sm);
+    if (e != hipSuccess) return MOE_ERR_HIP;
     tr.mark(sm, 5);
+    e = moe::launch_dw2(a, As, dO, dW2, vws, sm);
+    tr.mark(sm, 6);
     return hip_status(e);
   }
   // Untraced: the weight-gradient plans, which need only the routing, run

@@ -27,7 +27,7 @@ ROUTE_KERNELS = ("route_topk", "route_count", "route_select", "route_tslots")
 FWD_KERNELS = ("up_swiglu", "down", "aggregate_O")
 ROUTER_FWD_KERNELS = ("router_logits",)
 ROUTER_BWD_KERNELS = ("router_dlogits", "router_dx", "router_dw", "router_dw_reduce")
-BWD_KERNELS = ("dh", "dxt", "aggregate_dX", "dw1", "dw2")
+BWD_KERNELS = ("dw_plan", "dh", "dxt", "aggregate_dX", "dw1", "dw2")
 
 
 class Problem(ctypes.Structure):

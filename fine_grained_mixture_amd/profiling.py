@@ -126,7 +126,11 @@ def kernel_sources_sha256(root=ROOT):
 
 def _base_name(kernel_name):
     m = re.search(r"(k_\w+|route_\w+|__amd_rocclr_\w+)", kernel_name)
-    return m.group(1) if m else kernel_name
+    if not m:
+        return kernel_name
+    if m.group(1) == "k_dw_p":  # one template for both: dW1 gathers A (X), dW2 gathers B (dO)
+        return "k_dw1" if re.search(r"k_dw_p<.*,\s*true,\s*false>", kernel_name) else "k_dw2"
+    return m.group(1)
 
 
 def counter_per_dispatch(path, counter):

@@ -128,10 +128,10 @@ typedef struct {
  * records trace->events[i] (hipEvent_t, created by the caller) on `stream`
  * before its i-th kernel and trace->events[kernels] after the last one.
  * moe_route launches 4 kernels (top-K, counts, selection with the offset
- * scan, token CSR), moe_fwd 3, moe_bwd 5 (dH, dX-tilde,
- * dX aggregate, dW1, dW2; the dW segments include the chunk plan and the
- * reduction of split experts), moe_router_fwd 1, moe_router_bwd 4 (dlogits,
- * router dX, dWr partials, dWr reduction).  NULL disables tracing.
+ * scan, token CSR), moe_fwd 3, moe_bwd 6 segments (the weight-gradient chunk
+ * plans and schedules, dH, dX-tilde, dX aggregate, dW1, dW2; the dW segments
+ * include the reduction of split experts), moe_router_fwd 1, moe_router_bwd 4
+ * (dlogits, router dX, dWr partials, dWr reduction).  NULL disables tracing.
  */
 typedef struct {
   void **events;
