@@ -61,8 +61,25 @@ KERNEL_LABELS = {
     # persistent launches of the same steps
     "k_down_p": "down", "k_dxt_p": "dxt", "k_dxt_r": "dxt",
 }
-# the aggregation kernel runs twice per step: forward (O), then backward (dX)
+# kernels launched twice per step, labelled by launch order: the aggregation
+# (forward O, then backward dX) and the persistent weight-gradient kernel
+# (dW1, then dW2) when rocprofv3 truncates its template arguments
 AGGREGATE_LABELS = ("aggregate_O", "aggregate_dX")
+TWICE = {"k_aggregate": AGGREGATE_LABELS, "k_dw_p": ("dw1", "dw2")}
+
+
+class _Labeller:
+    """Step labels of base kernel names, fed in dispatch order."""
+
+    def __init__(self):
+        self.seen = collections.Counter()
+
+    def __call__(self, k):
+        if k in TWICE:
+            lab = TWICE[k][self.seen[k] % 2]
+            self.seen[k] += 1
+            return lab
+        return KERNEL_LABELS.get(k, k)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 NUM_XCD, NUM_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
@@ -128,7 +145,8 @@ def _base_name(kernel_name):
     m = re.search(r"(k_\w+|route_\w+|__amd_rocclr_\w+)", kernel_name)
     if not m:
         return kernel_name
-    if m.group(1) == "k_dw_p":  # one template for both: dW1 gathers A (X), dW2 gathers B (dO)
+    if m.group(1) == "k_dw_p" and "<" in kernel_name:
+        # one template for both steps: dW1 gathers A (X), dW2 gathers B (dO)
         return "k_dw1" if re.search(r"k_dw_p<.*,\s*true,\s*false>", kernel_name) else "k_dw2"
     return m.group(1)
 
@@ -143,14 +161,9 @@ def counter_per_dispatch(path, counter):
                              float(r["Counter_Value"])))
     rows.sort()
     out = collections.defaultdict(list)
-    n_agg = 0
+    label = _Labeller()
     for _, k, v in rows:
-        if k == "k_aggregate":
-            k = AGGREGATE_LABELS[n_agg % 2]
-            n_agg += 1
-        else:
-            k = KERNEL_LABELS.get(k, k)
-        out[k].append(v)
+        out[label(k)].append(v)
     return out
 
 
@@ -209,7 +222,32 @@ def _stats_md(path, cmd):
            "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in rows:
         out.append(f"| {name} | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    trace = os.path.join(os.path.dirname(path), "run_kernel_trace.csv")
+    split = _split_twice(trace) if os.path.exists(trace) else {}
+    if split:
+        out += ["", "Kernels launched twice per step, by launch order (from the per-dispatch "
+                "trace of the same run):", "",
+                "| step | kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+        for lab, (k, v) in split.items():
+            out.append(f"| {lab} | {k} | {len(v)} | {_mean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     return "\n".join(out) + "\n"
+
+
+def _split_twice(trace_csv):
+    """{step label: (kernel, [us per launch])} of the kernels in TWICE."""
+    rows = []
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            k = _base_name(r["Kernel_Name"])
+            if k in TWICE:
+                rows.append((int(r["Dispatch_Id"]), k,
+                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    label = _Labeller()
+    out = {}
+    for _, k, us in rows:
+        out.setdefault(label(k), (k, []))[1].append(us)
+    return out
 
 
 def mfma_table(counters_csv):
@@ -224,15 +262,9 @@ def mfma_table(counters_csv):
             d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
             d[r["Counter_Name"]] = float(r["Counter_Value"])
     per = collections.defaultdict(list)
-    n_agg = 0
+    label = _Labeller()
     for _, d in sorted(rows.items()):
-        k = d["name"]
-        if k == "k_aggregate":
-            k = AGGREGATE_LABELS[n_agg % 2]
-            n_agg += 1
-        else:
-            k = KERNEL_LABELS.get(k, k)
-        per[k].append(d)
+        per[label(d["name"])].append(d)
     out = {}
     for k, ds in per.items():
         out[k] = (len(ds), _mean([d["dur"] for d in ds]),
@@ -321,14 +353,9 @@ def pipeline_table(csvs):
                 d["name"] = _base_name(r["Kernel_Name"])
                 d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
                 d[r["Counter_Name"]] = float(r["Counter_Value"])
-        n_agg = 0
+        label = _Labeller()
         for _, d in sorted(rows.items()):
-            k = d["name"]
-            if k == "k_aggregate":
-                k = AGGREGATE_LABELS[n_agg % 2]
-                n_agg += 1
-            else:
-                k = KERNEL_LABELS.get(k, k)
+            k = label(d["name"])
             durs[k].append(d["dur"])
             for c, v in d.items():
                 if c not in ("name", "dur"):

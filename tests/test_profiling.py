@@ -99,3 +99,25 @@ def test_pipeline_summary_from_counters(tmp_path):
         cmd = ["run 1", "run 2"]
     row = [l for l in profiling._pipeline_md(Args).splitlines() if l.startswith("| dxt |")]
     assert row == ["| dxt | 500.0 | 500 | 0.100 | 50 | 0.75 | 900 | 0.50 | 0.75 | 0.40 | 0.25 |"]
+
+
+def test_twice_launched_kernels_split_by_launch_order(tmp_path):
+    # with truncated names the two launches of the persistent weight-gradient
+    # kernel (dW1, then dW2) and of the aggregation (O, then dX) are told
+    # apart by their order in each step
+    p = tmp_path / "run_kernel_trace.csv"
+    rows = ["Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp"]
+    seq = [("k_aggregate", 80), ("k_dw_p", 200), ("k_aggregate", 81), ("k_dw_p", 110)] * 2
+    t = 0
+    for i, (k, us) in enumerate(seq):
+        rows.append(f"{i + 1},{k},{t},{t + us * 1000}")
+        t += us * 1000 + 5000
+    p.write_text("\n".join(rows) + "\n")
+    split = profiling._split_twice(str(p))
+    assert {k: (v[0], v[1]) for k, v in split.items()} == {
+        "aggregate_O": ("k_aggregate", [80.0, 80.0]), "dw1": ("k_dw_p", [200.0, 200.0]),
+        "aggregate_dX": ("k_aggregate", [81.0, 81.0]), "dw2": ("k_dw_p", [110.0, 110.0])}
+    # full names carry the gathered operand in the template arguments
+    assert profiling._base_name("k_dw_p<moe::TileCfg<unsigned short, 256>, true, false>(x)") == "k_dw1"
+    assert profiling._base_name("k_dw_p<moe::TileCfg<unsigned short, 256>, false, true>(x)") == "k_dw2"
+    assert profiling._base_name("k_dw_p") == "k_dw_p"
