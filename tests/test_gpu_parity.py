@@ -63,6 +63,10 @@ EXTRA = {
     "d2048_n64": LayerShape("d2048_n64", 700, 2048, 64, 16, 2, 64, "fan_in", "normal_bias"),
     # ... and d past 2048: dX-tilde per tile, the down-projection persistent
     "d2304": LayerShape("d2304", 640, 2304, 128, 8, 2, 32, "fan_in", "iid"),
+    # the persistent weight-gradient kernels with more output tiles per item
+    # than workgroups per XCD (48 for dW1 on 256 x 256 tiles, 48 for dW2 on
+    # 128 x 256), so one workgroup gets several tiles of an item
+    "d4096_n384": LayerShape("d4096_n384", 400, 4096, 384, 6, 2, 32, "fan_in", "normal_bias"),
 }
 KIND = {torch.bfloat16: "bf16", torch.float32: "f32"}
 ORC_MODE = {"tc": orc.TC, "tr": orc.TR, "tr_up": orc.TR_UP, "tr_down": orc.TR_DOWN,
@@ -188,6 +192,7 @@ def nonfinite_logits(logits, seed=7):
 
 SMALL_CASES = SMALL_CASES + [
     ("d2048_n64", torch.bfloat16, "tr"), ("d2304", torch.bfloat16, "tc"),
+    ("d4096_n384", torch.bfloat16, "tr"),
     ("long_t", torch.bfloat16, "tr"), ("long_t", torch.bfloat16, "tc"),
     ("long_t", torch.bfloat16, "tr_stochastic"),
     ("k32", torch.bfloat16, "tr"), ("k32", torch.float32, "tc"),
