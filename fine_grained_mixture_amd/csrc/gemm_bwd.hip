@@ -547,7 +547,7 @@ __device__ __forceinline__ void sched_one(const int* __restrict__ header,
     const int x = wave, b = x + 8 * lane, nx = xn[x];
     int key = lane < 32 ? lane : INT_MAX;  // work << 5 | l
     int c = 0;                             // entries of b's list
-    int* const mine = list + int64_t(b) * cap;
+    int* const mine = list + int64_t(lane < 32 ? b : 0) * cap;  // lanes past 31 write nothing
     for (int k0 = 0; k0 < nx; k0 += 64) {
       const int iv = k0 + lane < nx ? xl[x][k0 + lane] : 0;
       const int cv = k0 + lane < nx ? cost[iv] : 0;
