@@ -405,7 +405,7 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(collectives and sharding are out of scope); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)

@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID = -1,     /* null / misaligned pointer, bad dimension     */
-  MOE_ERR_UNSUPPORTED = -2, /* valid problem this build does not handle     */
+  MOE_ERR_UNSUPPORTED = -2, /* valid problem the library does not handle   */
   MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_sizes reports     */
   MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed   */
 } moe_status;
@@ -147,7 +147,7 @@ typedef struct {
  * O, dX (T x d); H, dH (slot_cap x 2n); Y, dX-tilde (slot_cap x d); one
  * expert of W1 (d x 2n) or W2 (n x d); Wr (E x d); logits (T x E fp32); the
  * router backward's padded copy of dlogits (T x ceil(E/128)*128).
- * Why these limits: the tile shapes of this build cover d in multiples of
+ * Why these limits: the library's tile shapes cover d in multiples of
  * 128 and the listed n (the GEMM tiles take whole 128-column slabs of d and
  * whole gate/up halves of n); the routing kernels keep one token's experts
  * and one expert's ranking state in a workgroup (K <= 32, E <= 1024). */

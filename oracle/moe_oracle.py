@@ -15,7 +15,7 @@ here are that plain definition written out in fp64 numpy, one expert at a
 time.  The one step that is an algorithm rather than a closed form, token
 rounding, follows the notes' key design 1 step by step.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * gate = softmax over all E experts of the fp32 logits, computed in fp64;
     the top-K gate weights are NOT renormalised (s = p);
   * top-K ties go to the lower expert index (decided on the fp32 logits);
